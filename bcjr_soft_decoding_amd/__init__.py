@@ -1,0 +1,9 @@
+"""BCJR soft trellis decoding on MI355X (gfx950).
+
+The work is done by hand-written HIP kernels behind the C ABI declared in ``include/bcjr.h``
+(``libbcjr.so``); ``bcjr_soft_decoding_amd.bcjr`` is the thin ctypes binding over it and
+``bcjr_soft_decoding_amd.autograd`` wraps it as a differentiable soft quantiser.
+The library is loaded on first use, and a missing library is an error, never a fallback.
+"""
+
+__all__ = ["bcjr", "synth"]
