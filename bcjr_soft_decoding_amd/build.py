@@ -1,0 +1,63 @@
+"""Build the HIP library ``libbcjr.so`` for gfx950 in-tree (no JIT cache).
+
+    python -m bcjr_soft_decoding_amd.build
+
+Every source under ``csrc/`` is compiled with hipcc for gfx950 only, with packed-fp32
+instruction selection disabled, and linked into ``bcjr_soft_decoding_amd/_lib/libbcjr.so``.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT_DIR = os.path.join(PKG, "_lib")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(OUT_DIR, "libbcjr.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result", "-Wno-unknown-pragmas",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    # the host pass does not know the gfx950 target feature; that warning is expected
+    errs = [ln for ln in r.stderr.splitlines() if "warning" in ln and "packed-fp32-ops" not in ln]
+    if errs:
+        sys.stderr.write("\n".join(errs) + "\n")
+    return obj
+
+
+def build(jobs: int = 8) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,160 @@
+// Host layer of the C ABI (include/bcjr.h): argument validation, size queries and dispatch.
+// Every check runs before anything touches the HIP runtime, so the error paths need no device.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "bcjr.h"
+#include "geom.h"
+#include "internal.h"
+
+namespace bcjr {
+
+bool sparse_geom(int n, int k, int64_t B, SparseGeom* g) {
+  if (!geom_supported(n, k) || !sparse_shape_built(n, k)) return false;
+  g->n = n;
+  g->k = k;
+  g->K = 1 << k;
+  g->S = 1 << n;
+  g->M = g->S / g->K;
+  g->NG = geom_ng(n, k);
+  g->G = geom_g(n, k);
+  g->LPS = geom_lps(n, k);
+  g->SPB = geom_spb(n, k);
+  g->BLOCK = geom_block(n, k);
+  g->units = B > 0 ? (B + g->SPB - 1) / g->SPB : 0;
+  const int64_t mx = geom_max_slots(n, k);
+  g->slots = g->units < mx ? g->units : mx;
+  return true;
+}
+
+size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L) {
+  return (size_t)g.slots * sparse_fwd_slot_bytes(g, L);
+}
+size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L) {
+  return (size_t)g.slots * sparse_bwd_slot_bytes(g, L) + round256((size_t)g.slots * g.S * sizeof(float));
+}
+size_t sparse_vit_ws_bytes(const SparseGeom& g, int64_t L) {
+  return round256((size_t)g.slots * L * g.BLOCK * (g.K * g.G));
+}
+
+}  // namespace bcjr
+
+using namespace bcjr;
+
+namespace {
+
+bool shape_ok(const bcjr_trellis* tr) {
+  return tr->state_bits >= 1 && tr->state_bits <= 16 && tr->bits_per_step >= 1 &&
+         tr->bits_per_step <= tr->state_bits;
+}
+
+// Common validation. On success fills *g (for B > 0) and returns BCJR_OK.
+bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, SparseGeom* g) {
+  if (tr == nullptr) return BCJR_E_ARG;
+  if (!shape_ok(tr) || B < 0 || L < 1) return BCJR_E_SHAPE;
+  if (tr->weights_per_step != 1) return BCJR_E_UNSUPPORTED;
+  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, g)) return BCJR_E_UNSUPPORTED;
+  if (B > 0 && tr->codebook == nullptr) return BCJR_E_ARG;
+  return BCJR_OK;
+}
+
+bool temp_ok(float T) { return isfinite(T) && T > 0.0f; }
+
+// Workspaces are accessed with 16-byte vector loads and stores.
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  return ws != nullptr && have >= need && ((uintptr_t)ws & 15) == 0;
+}
+
+bcjr_status from_hip(int e) { return e == 0 ? BCJR_OK : BCJR_E_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int bcjr_supported(const bcjr_trellis* tr) {
+  if (tr == nullptr || !shape_ok(tr) || tr->weights_per_step != 1) return 0;
+  SparseGeom g;
+  return sparse_geom(tr->state_bits, tr->bits_per_step, 1, &g) ? 1 : 0;
+}
+
+size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L) {
+  if (tr == nullptr || !shape_ok(tr) || B < 0 || L < 1) return 0;
+  return round256(bcjr::saved_bytes(B, L));
+}
+
+size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int which) {
+  if (tr == nullptr || !shape_ok(tr) || B < 0 || L < 1 || tr->weights_per_step != 1) return 0;
+  SparseGeom g;
+  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, &g)) return 0;
+  if (B == 0) return 0;
+  switch (which) {
+    case 0: return sparse_fwd_ws_bytes(g, L);
+    case 1: return sparse_bwd_ws_bytes(g, L);
+    case 2: return sparse_vit_ws_bytes(g, L);
+    default: return 0;
+  }
+}
+
+bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
+                         float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,
+                         bcjr_stream_t stream) {
+  SparseGeom g;
+  bcjr_status st = check_common(tr, B, L, &g);
+  if (st != BCJR_OK) return st;
+  if (!temp_ok(T)) return BCJR_E_ARG;
+  if (B == 0) return BCJR_OK;
+  if (!w || !w_hat || !log_z || !saved) return BCJR_E_ARG;
+  const size_t need = sparse_fwd_ws_bytes(g, L);
+  if (!ws_ok(ws, ws_bytes, need)) return BCJR_E_WORKSPACE;
+  return from_hip(launch_sparse_forward(g, tr->codebook, w, B, L, T, w_hat, log_z,
+                                        static_cast<float*>(saved), ws, stream));
+}
+
+bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
+                          const void* saved, const float* grad_w_hat, const float* grad_log_z,
+                          float* grad_w, float* grad_codebook, void* ws, size_t ws_bytes,
+                          bcjr_stream_t stream) {
+  SparseGeom g;
+  bcjr_status st = check_common(tr, B, L, &g);
+  if (st != BCJR_OK) return st;
+  if (!temp_ok(T)) return BCJR_E_ARG;
+  if (grad_codebook == nullptr) return BCJR_E_ARG;
+  if (B == 0) {
+    // no chain contributes: the summed codebook gradient is zero
+    return from_hip(launch_fill_zero(grad_codebook, (int64_t)1 << tr->state_bits, stream));
+  }
+  if (!w || !saved || !grad_w_hat || !grad_w) return BCJR_E_ARG;
+  const size_t need = sparse_bwd_ws_bytes(g, L);
+  if (!ws_ok(ws, ws_bytes, need)) return BCJR_E_WORKSPACE;
+  return from_hip(launch_sparse_backward(g, tr->codebook, w, B, L, T,
+                                         static_cast<const float*>(saved), grad_w_hat, grad_log_z,
+                                         grad_w, grad_codebook, ws, stream));
+}
+
+bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                           int32_t* states, float* w_hard, void* ws, size_t ws_bytes,
+                           bcjr_stream_t stream) {
+  SparseGeom g;
+  bcjr_status st = check_common(tr, B, L, &g);
+  if (st != BCJR_OK) return st;
+  if (B == 0) return BCJR_OK;
+  if (!w || !states) return BCJR_E_ARG;
+  const size_t need = sparse_vit_ws_bytes(g, L);
+  if (!ws_ok(ws, ws_bytes, need)) return BCJR_E_WORKSPACE;
+  return from_hip(launch_viterbi(g, tr->codebook, w, B, L, states, w_hard, ws, stream));
+}
+
+const char* bcjr_status_string(bcjr_status s) {
+  switch (s) {
+    case BCJR_OK: return "ok";
+    case BCJR_E_ARG: return "invalid argument (null pointer, bad temperature or flag)";
+    case BCJR_E_SHAPE: return "invalid shape (n, k, B or L out of range)";
+    case BCJR_E_WORKSPACE: return "workspace missing or smaller than the size query";
+    case BCJR_E_DEVICE: return "HIP runtime or kernel launch error";
+    case BCJR_E_UNSUPPORTED: return "valid shape with no kernel built for it";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

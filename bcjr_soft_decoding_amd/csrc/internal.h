@@ -1,0 +1,70 @@
+// Internal declarations shared by the host layer (host.cpp) and the kernel files (*.hip).
+// Nothing here is part of the public ABI (include/bcjr.h).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bcjr.h"
+
+namespace bcjr {
+
+// Launch geometry of one bitshift configuration (n, k). Every quantity is a pure function of
+// (n, k, B, L), so workspace sizes can be queried without a device.
+struct SparseGeom {
+  int n, k;      // state bits, bits per step
+  int K;         // 1 << k branches
+  int S;         // 1 << n states
+  int M;         // S / K butterflies (forward messages per step)
+  int NG;        // S / K^2 groups of K x K states
+  int G;         // groups per lane
+  int LPS;       // lanes per chain
+  int SPB;       // chains per block (LPS < 64: 64 / LPS, else 1)
+  int BLOCK;     // threads per block
+  int64_t units; // ceil(B / SPB)
+  int64_t slots; // blocks launched (= workspace slots)
+};
+
+// True if kernels for (n, k) are compiled into the library (sparse_kernels.hip).
+bool sparse_shape_built(int n, int k);
+
+// Returns false if no kernel is built for (n, k).
+bool sparse_geom(int n, int k, int64_t B, SparseGeom* g);
+
+// Layout of the forward -> backward context: log2 Z of every chain as a double [B] (padded to
+// a multiple of 32 doubles), then the soft codeword w_hat [B, L] in fp32.
+// saved_what_offset() is in floats.
+inline int64_t saved_what_offset(int64_t B) { return 2 * ((B + 31) / 32 * 32); }
+inline size_t saved_bytes(int64_t B, int64_t L) {
+  return (size_t)(saved_what_offset(B) + B * L) * sizeof(float);
+}
+
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace layout of the sparse kernels: one slot per persistent block. A forward slot holds
+// the lam history [L][BLOCK][K*G] with 8-byte entries and the shift prefix [L][SPB] (double);
+// a backward slot adds the Phi history [L][BLOCK][K*G] (fp32); the backward workspace ends
+// with the codebook-gradient partials [slots][S] (fp32). Sizes do not depend on T.
+inline size_t sparse_fwd_slot_bytes(const SparseGeom& g, int64_t L) {
+  return round256((size_t)L * g.BLOCK * (g.K * g.G) * 8 + (size_t)L * g.SPB * 8);
+}
+inline size_t sparse_bwd_slot_bytes(const SparseGeom& g, int64_t L) {
+  return round256((size_t)L * g.BLOCK * (g.K * g.G) * 12 + (size_t)L * g.SPB * 8);
+}
+size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L);
+size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L);
+size_t sparse_vit_ws_bytes(const SparseGeom& g, int64_t L);
+
+// Kernel launchers (defined in sparse_kernels.hip / viterbi_kernels.hip). They assume every
+// argument was validated by the host layer. Return a hipError_t as int.
+int launch_sparse_forward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
+                          int64_t L, float T, float* w_hat, float* log_z, float* saved_logz2,
+                          void* ws, void* stream);
+int launch_sparse_backward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
+                           int64_t L, float T, const float* saved_logz2, const float* grad_w_hat,
+                           const float* grad_log_z, float* grad_w, float* grad_codebook, void* ws,
+                           void* stream);
+int launch_fill_zero(float* dst, int64_t count, void* stream);
+int launch_viterbi(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
+                   int64_t L, int32_t* states, float* w_hard, void* ws, void* stream);
+
+}  // namespace bcjr

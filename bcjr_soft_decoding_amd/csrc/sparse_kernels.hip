@@ -1,0 +1,765 @@
+// Forward-backward kernels for the bitshift trellis on gfx950.
+//
+// Method: the BCJR forward-backward sum-product recursion at temperature T of "BCJR-QAT: A
+// Differentiable Relaxation of Trellis-Coded Weight Quantization" (abstract; gist.science
+// technical summary, "Core mechanism" and "Key technical innovations"): Boltzmann posteriors
+// over trellis paths, the soft codeword w_hat_t = sum_s c(s) p_T(s_t = s | w), log Z, and the
+// exact gradient of sum_t g_t w_hat_t + h log Z with respect to w and the codebook.
+//
+// Arithmetic is in base-2 log units: the emission log2-potential is
+// ell_t(s) = -(log2(e)/T) (w_t - c(s))^2.
+//
+// Factorisation used here (exact, a property of the bitshift trellis): the K successors
+// s' = K*j + b of butterfly j share the predecessors j + a*M, so the forward message is one
+// number per butterfly,
+//     alpha_t(s) = ell_t(s) + lam_t(s >> k),   lam_{t+1}(j) = LSE_a alpha_t(j + a*M),
+// and likewise beta_t(s) = rho_t(s mod M), rho_{t-1}(j) = LSE_b [ell_t(K*j+b) + rho_t((K*j+b) mod M)].
+// Each LSE is evaluated once per butterfly instead of once per state: one exp2 per
+// state-step and one log2 per butterfly-step per direction. See geom.h for the K x K block
+// layout that makes both recursions lane-local.
+//
+// Normalisation: after every step the messages are shifted by the integer floor of their
+// chain-wide maximum. The integer shifts are summed exactly, and log2 Z is kept next to them
+// in double precision, so the per-step posterior normaliser
+// log2 Z - (forward shifts up to t) - (backward shifts down to t) carries no rounding drift.
+//
+// Precision policies. The messages lam and rho are sums along the trellis of emission terms
+// whose size grows like 1/T. In fp32 their accumulated rounding (about an ulp of a value of
+// size log2(e)/T per step) limits the gradient, whose sensitivity to posterior errors is
+// large when T is small, so below T = 0.05 the messages are carried in fp64 and the emission
+// is formed from the unscaled difference w - c; exponentials, the posterior weights and the
+// conditional expectations stay fp32 in both policies. The 2^16-state trellis keeps fp32
+// messages at every T: its fp64 backward messages would not fit in LDS.
+//
+// One persistent block per workspace slot loops over chain units. Phase A runs the forward
+// recursion and stores each lane's column offsets lam_t(x + a*NG) (the alpha-side inputs of
+// its K x K blocks) in the slot's history; phase B runs the backward recursion, reads the
+// history back in reverse and forms posteriors, the soft codeword and the gradients.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "geom.h"
+#include "internal.h"
+
+namespace bcjr {
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr double kLog2e = 1.4426950408889634074;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+// Reciprocal refined by one Newton step: the conditional expectations below are weighted
+// averages carried along the whole chain, so the weights must sum to one to within rounding.
+__device__ __forceinline__ float rcp_nr(float x) {
+  const float r = __builtin_amdgcn_rcpf(x);
+  return __builtin_fmaf(__builtin_fmaf(-x, r, 1.0f), r, r);
+}
+
+// fp32 messages; emission -(u - v)^2 with u = q w, v = q c, q = sqrt(log2(e)/T).
+struct Fast {
+  using MT = float;
+  static constexpr bool kPrecise = false;
+};
+// fp64 messages; emission -kappa (w - c)^2 with kappa = log2(e)/T applied in fp64.
+struct Precise {
+  using MT = double;
+  static constexpr bool kPrecise = true;
+};
+
+// Per-call constants: per-state values v = sc * c, per-step u = sc * w, c = csc * v.
+struct Consts {
+  float sc, csc;
+  double kap;   // log2(e)/T (used by the precise emission)
+  float inv_t;  // 1/T
+};
+
+template <class P>
+__device__ __forceinline__ typename P::MT emit(float u, float v, typename P::MT off, double kap) {
+  const float d = u - v;
+  if constexpr (P::kPrecise) {
+    const double dd = (double)d;
+    return __builtin_fma(-(kap * dd), dd, off);
+  } else {
+    (void)kap;
+    return __builtin_fmaf(-d, d, off);
+  }
+}
+template <class T>
+__device__ __forceinline__ T tmax(T a, T b) { return a > b ? a : b; }
+
+template <int K_, int G_, int LPS_, class P_, bool BWD_>
+struct Cfg {
+  using P = P_;
+  using MT = typename P_::MT;
+  static constexpr int K = K_, G = G_, LPS = LPS_;
+  static constexpr bool BWD = BWD_;
+  static constexpr int NG = G * LPS;  // K x K blocks per chain
+  static constexpr int M = K * NG;    // butterflies per chain
+  static constexpr int S = K * M;     // states
+  static constexpr int KG = K * G;    // message values a lane reads per step
+  static constexpr int SPB = LPS < 64 ? 64 / LPS : 1;
+  static constexpr int BLOCK = LPS < 64 ? 64 : LPS;
+  static constexpr int NWAVES = BLOCK / 64;
+  // LDS per buffer: the MT message (+ the fp32 expectation message in the backward).
+  static constexpr long long BUF_BYTES = (long long)SPB * M * ((long long)sizeof(MT) + (BWD ? 4 : 0));
+  // Double-buffer the message arrays when both buffers fit in 128 KiB, else one buffer and a
+  // second barrier per step.
+  static constexpr bool DB = 2 * BUF_BYTES <= 128 * 1024;
+  static constexpr int NBUF = DB ? 2 : 1;
+};
+
+// Reduction over aligned groups of W lanes inside a wave (xor butterfly: every lane of the
+// group ends with the bitwise-identical result).
+template <int W, class T>
+__device__ __forceinline__ T lanes_reduce(T v, bool is_max) {
+#pragma unroll
+  for (int o = W / 2; o >= 1; o >>= 1) {
+    const T o2 = __shfl_xor(v, o, 64);
+    v = is_max ? tmax(v, o2) : v + o2;
+  }
+  return v;
+}
+
+// Chain-wide reduction of NV values (MASK bit i set = max, clear = sum). Includes one
+// workgroup barrier, which also publishes any LDS message writes made before the call.
+// For chains wider than a wave the per-wave partials go through `red` (double-buffered by
+// `rp`) and are combined in wave order, so every lane gets the same bits.
+template <class C, int NV, unsigned MASK, class T>
+__device__ __forceinline__ void chain_reduce(T (&v)[NV], double* red, int& rp) {
+  if constexpr (C::LPS <= 64) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = lanes_reduce<C::LPS>(v[i], (MASK >> i) & 1u);
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = lanes_reduce<64>(v[i], (MASK >> i) & 1u);
+    double* r = red + rp * (C::NWAVES * 4);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) r[wave * 4 + i] = (double)v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      T acc = (T)r[i];
+      for (int wv = 1; wv < C::NWAVES; ++wv)
+        acc = ((MASK >> i) & 1u) ? tmax(acc, (T)r[wv * 4 + i]) : acc + (T)r[wv * 4 + i];
+      v[i] = acc;
+    }
+    rp ^= 1;
+  }
+}
+
+// Vector copies between registers and memory (LDS or global), 16 bytes at a time.
+template <int N, class T>
+__device__ __forceinline__ void store_vec(T* __restrict__ dst, const T* src) {
+  constexpr int V = 16 / (int)sizeof(T);
+  if constexpr (N % V == 0) {
+    using Vec = __attribute__((ext_vector_type(V))) T;
+#pragma unroll
+    for (int i = 0; i < N; i += V) {
+      Vec x;
+#pragma unroll
+      for (int j = 0; j < V; ++j) x[j] = src[i + j];
+      *reinterpret_cast<Vec*>(dst + i) = x;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = src[i];
+  }
+}
+template <int N, class T>
+__device__ __forceinline__ void load_vec(const T* __restrict__ src, T* dst) {
+  constexpr int V = 16 / (int)sizeof(T);
+  if constexpr (N % V == 0) {
+    using Vec = __attribute__((ext_vector_type(V))) T;
+#pragma unroll
+    for (int i = 0; i < N; i += V) {
+      const Vec x = *reinterpret_cast<const Vec*>(src + i);
+#pragma unroll
+      for (int j = 0; j < V; ++j) dst[i + j] = x[j];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = src[i];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Forward: soft codeword and log Z.
+// ---------------------------------------------------------------------------------------------
+template <class C>
+__global__ void __launch_bounds__(C::BLOCK)
+k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long long B, long long L,
+             Consts k, float* __restrict__ w_hat, float* __restrict__ log_z,
+             double* __restrict__ saved_lz, float* __restrict__ saved_what, void* __restrict__ ws,
+             size_t slot_bytes, long long units) {
+  using P = typename C::P;
+  using MT = typename C::MT;
+  constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
+  constexpr int SPB = C::SPB, BLOCK = C::BLOCK;
+  __shared__ __attribute__((aligned(16))) MT msg[C::NBUF][SPB * M];
+  __shared__ double red[2 * C::NWAVES * 4];
+
+  const int tid = threadIdx.x;
+  const int q = LPS < 64 ? tid / LPS : 0;    // chain within the block
+  const int p = LPS < 64 ? tid % LPS : tid;  // lane within the chain
+
+  float V[G][K][K];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int r = 0; r < K; ++r)
+#pragma unroll
+      for (int a = 0; a < K; ++a) V[g][r][a] = k.sc * cb[K * (p + g * LPS) + r + a * M];
+
+  // slot layout: lam history [L][BLOCK][KG] (8-byte entries), shift prefix N [L][SPB] (double)
+  char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
+  MT* __restrict__ hs = reinterpret_cast<MT*>(sb);
+  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)L * BLOCK * KG * 8);
+  int mb = 0, rp = 0;
+
+  for (long long unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const long long b = unit * SPB + q;
+    const bool valid = b < B;
+    const float* __restrict__ wb = w + (valid ? b : B - 1) * L;
+
+    // ---- phase A: forward messages lam, t = 0 .. L-1 -------------------------------------
+    MT lc[G][K];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int a = 0; a < K; ++a) lc[g][a] = (MT)0;
+    double N = 0.0, lz2 = 0.0;
+    for (long long t = 0; t < L; ++t) {
+      store_vec<KG>(hs + ((size_t)t * BLOCK + tid) * KG, &lc[0][0]);
+      if (p == 0) ns[t * SPB + q] = N;
+      const float u = k.sc * wb[t];
+      MT out[G][K];
+      MT mx = (MT)-INFINITY;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          MT x[K];
+          MT m = (MT)-INFINITY;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            x[a] = emit<P>(u, V[g][r][a], lc[g][a], k.kap);
+            m = tmax(m, x[a]);
+          }
+          float s = 0.f;
+#pragma unroll
+          for (int a = 0; a < K; ++a) s += ex2((float)(x[a] - m));
+          out[g][r] = m + (MT)lg2(s);
+          mx = tmax(mx, out[g][r]);
+        }
+      if (t == L - 1) {
+        MT v1[1] = {mx};
+        chain_reduce<C, 1, 1u>(v1, red, rp);
+        float s2 = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < K; ++r) s2 += ex2((float)(out[g][r] - v1[0]));
+        float v2[1] = {s2};
+        chain_reduce<C, 1, 0u>(v2, red, rp);
+        lz2 = N + ((double)v1[0] + (double)lg2(v2[0]));
+        break;
+      }
+      MT* mw = msg[mb] + q * M;
+#pragma unroll
+      for (int g = 0; g < G; ++g) store_vec<K>(mw + K * (p + g * LPS), out[g]);
+      MT v1[1] = {mx};
+      chain_reduce<C, 1, 1u>(v1, red, rp);
+      const MT sh = floor(v1[0]);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) lc[g][a] = mw[p + g * LPS + a * NG] - sh;
+      N += (double)sh;
+      if constexpr (C::DB) mb ^= 1; else __syncthreads();
+    }
+    __syncthreads();  // phase-A history writes (incl. other lanes' N) visible to phase B
+
+    // ---- phase B: backward messages rho, posterior and soft codeword, t = L-1 .. 0 -------
+    MT rr[G][K];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int r = 0; r < K; ++r) rr[g][r] = (MT)0;
+    double Np = 0.0;
+    MT lcn[G][K];
+    load_vec<KG>(hs + ((size_t)(L - 1) * BLOCK + tid) * KG, &lcn[0][0]);
+    double Nn = ns[(L - 1) * SPB + q];
+    for (long long t = L - 1; t >= 0; --t) {
+      MT lcur[G][K];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) lcur[g][a] = lcn[g][a];
+      const double Nt = Nn;
+      if (t > 0) {
+        load_vec<KG>(hs + ((size_t)(t - 1) * BLOCK + tid) * KG, &lcn[0][0]);
+        Nn = ns[(t - 1) * SPB + q];
+      }
+      const float u = k.sc * wb[t];
+      const MT LZ = (MT)((lz2 - Nt) - Np);
+      float num = 0.f, den = 0.f;
+      MT mx = (MT)-INFINITY;
+      MT rout[G][K];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          MT y[K];
+          MT m = (MT)-INFINITY;
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            y[r] = emit<P>(u, V[g][r][a], rr[g][r], k.kap);
+            m = tmax(m, y[r]);
+          }
+          float cs = 0.f, cw = 0.f;
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            const float e = ex2((float)(y[r] - m));
+            cs += e;
+            cw = __builtin_fmaf(V[g][r][a], e, cw);
+          }
+          rout[g][a] = m + (MT)lg2(cs);
+          mx = tmax(mx, rout[g][a]);
+          const float f = ex2((float)((m + lcur[g][a]) - LZ));
+          num = __builtin_fmaf(f, cw, num);
+          den = __builtin_fmaf(f, cs, den);
+        }
+      MT* mw = msg[mb] + q * M;
+      if (t > 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int a = 0; a < K; ++a) mw[p + g * LPS + a * NG] = rout[g][a];
+      }
+      MT v3[3] = {(MT)num, (MT)den, mx};
+      chain_reduce<C, 3, 4u>(v3, red, rp);
+      if (valid && p == 0) {
+        const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
+        w_hat[b * L + t] = wh;
+        saved_what[b * L + t] = wh;
+      }
+      if (t == 0) break;
+      const MT sh = floor(v3[2]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        MT tmp[K];
+        load_vec<K>(mw + K * (p + g * LPS), tmp);
+#pragma unroll
+        for (int r = 0; r < K; ++r) rr[g][r] = tmp[r] - sh;
+      }
+      Np += (double)sh;
+      if constexpr (C::DB) mb ^= 1; else __syncthreads();
+    }
+    if (valid && p == 0) {
+      log_z[b] = (float)(lz2 * (double)kLn2);
+      saved_lz[b] = lz2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Backward: gradient of F = sum_t g_t w_hat_t + h log Z w.r.t. w and the codebook.
+// With the posterior written as a Markov chain, E[F | s_t = s] = Fwd_t(s) + g_t c(s) + Bwd_t(s)
+// where the conditional expectations obey the same butterfly factorisation as the messages:
+//   Fwd_t(s) = Phi_t(s >> k),  Phi_{t+1}(j)  = sum_a q(a|j) (Phi_t((j+aM)>>k) + g_t c(j+aM)),
+//   Bwd_t(s) = Psi_t(s mod M), Psi_{t-1}(j') = sum_b r(b|j') (Psi_t((Kj'+b) mod M) + g_t c(Kj'+b)),
+// q and r being the softmax weights of the forward / backward LSEs (no extra exponentials).
+// D_t(s) = gamma_t(s) (E[F | s_t = s] - E[F]). The recursions carry the centred codeword
+// c(s) - w_hat_t (w_hat from the forward): Phi and Psi then hold conditional expectations of
+// sum_u g_u (c(s_u) - w_hat_u), which are small wherever the posterior is sharp, E[F] drops
+// out (its centred value is 0), and D_t(s) = gamma_t(s) (Phi + g_t (c(s) - w_hat_t) + Psi).
+// With E_t = D_t + h gamma_t:
+//   dF/dw_t  = (2/T) (sum_s c(s) E_t(s) - h w_t)
+//   dF/dc(s) = sum_t [ g_t gamma_t(s) + (2/T)(w_t - c(s)) E_t(s) ].
+// ---------------------------------------------------------------------------------------------
+template <class C>
+__global__ void __launch_bounds__(C::BLOCK)
+k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long long B, long long L,
+             Consts k, const double* __restrict__ saved_lz, const float* __restrict__ saved_what,
+             const float* __restrict__ gup, const float* __restrict__ hup,
+             float* __restrict__ grad_w, float* __restrict__ partial, void* __restrict__ ws,
+             size_t slot_bytes, long long units) {
+  using P = typename C::P;
+  using MT = typename C::MT;
+  constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
+  constexpr int SPB = C::SPB, BLOCK = C::BLOCK;
+  __shared__ __attribute__((aligned(16))) MT msgl[C::NBUF][SPB * M];
+  __shared__ __attribute__((aligned(16))) float msgp[C::NBUF][SPB * M];
+  __shared__ double red[2 * C::NWAVES * 4];
+
+  const int tid = threadIdx.x;
+  const int q = LPS < 64 ? tid / LPS : 0;
+  const int p = LPS < 64 ? tid % LPS : tid;
+  const float k2 = 2.0f * k.inv_t * k.csc;  // (2/T)(w - c) = k2 * (u - v)
+
+  float V[G][K][K], acc[G][K][K];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int r = 0; r < K; ++r)
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        V[g][r][a] = k.sc * cb[K * (p + g * LPS) + r + a * M];
+        acc[g][r][a] = 0.f;
+      }
+
+  // slot layout: lam history [L][BLOCK][KG] (8-byte entries), Phi history [L][BLOCK][KG]
+  // (fp32), shift prefix N [L][SPB] (double)
+  char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
+  MT* __restrict__ hl = reinterpret_cast<MT*>(sb);
+  float* __restrict__ hp = reinterpret_cast<float*>(sb + (size_t)L * BLOCK * KG * 8);
+  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)L * BLOCK * KG * 12);
+  int mb = 0, rp = 0;
+
+  for (long long unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const long long b = unit * SPB + q;
+    const bool valid = b < B;
+    const long long bb = valid ? b : B - 1;
+    const float* __restrict__ wb = w + bb * L;
+    const float* __restrict__ gb = gup + bb * L;
+    const float* __restrict__ whb = saved_what + bb * L;
+    const float h = (hup != nullptr && valid) ? hup[bb] : 0.f;
+    const double lz2 = saved_lz[bb];
+
+    // ---- phase A: lam and Phi, t = 0 .. L-1 ----------------------------------------------
+    MT lc[G][K];
+    float pc[G][K];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int a = 0; a < K; ++a) { lc[g][a] = (MT)0; pc[g][a] = 0.f; }
+    double N = 0.0;
+    for (long long t = 0; t < L; ++t) {
+      store_vec<KG>(hl + ((size_t)t * BLOCK + tid) * KG, &lc[0][0]);
+      store_vec<KG>(hp + ((size_t)t * BLOCK + tid) * KG, &pc[0][0]);
+      if (p == 0) ns[t * SPB + q] = N;
+      if (t == L - 1) break;
+      const float u = k.sc * wb[t];
+      const float gtp = gb[t] * k.csc;     // g_t c(s) = gtp * v(s)
+      const float gwh = gb[t] * whb[t];    // g_t w_hat_t
+      MT out[G][K];
+      float pout[G][K];
+      float pcc[G][K];  // Phi_t - g_t w_hat_t at the column offsets
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) pcc[g][a] = pc[g][a] - gwh;
+      MT mx = (MT)-INFINITY;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          MT x[K];
+          MT m = (MT)-INFINITY;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            x[a] = emit<P>(u, V[g][r][a], lc[g][a], k.kap);
+            m = tmax(m, x[a]);
+          }
+          float s = 0.f, ph = 0.f;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            const float e = ex2((float)(x[a] - m));
+            s += e;
+            ph = __builtin_fmaf(e, __builtin_fmaf(gtp, V[g][r][a], pcc[g][a]), ph);
+          }
+          out[g][r] = m + (MT)lg2(s);
+          pout[g][r] = ph * rcp_nr(s);
+          mx = tmax(mx, out[g][r]);
+        }
+      MT* mw = msgl[mb] + q * M;
+      float* pw = msgp[mb] + q * M;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        store_vec<K>(mw + K * (p + g * LPS), out[g]);
+        store_vec<K>(pw + K * (p + g * LPS), pout[g]);
+      }
+      MT v1[1] = {mx};
+      chain_reduce<C, 1, 1u>(v1, red, rp);
+      const MT sh = floor(v1[0]);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          lc[g][a] = mw[p + g * LPS + a * NG] - sh;
+          pc[g][a] = pw[p + g * LPS + a * NG];
+        }
+      N += (double)sh;
+      if constexpr (C::DB) mb ^= 1; else __syncthreads();
+    }
+    __syncthreads();
+
+    // ---- phase B: rho and Psi, posterior, D, gradients, t = L-1 .. 0 ---------------------
+    MT rr[G][K];
+    float qr[G][K];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int r = 0; r < K; ++r) { rr[g][r] = (MT)0; qr[g][r] = 0.f; }
+    double Np = 0.0;
+    MT lcn[G][K];
+    float pcn[G][K];
+    load_vec<KG>(hl + ((size_t)(L - 1) * BLOCK + tid) * KG, &lcn[0][0]);
+    load_vec<KG>(hp + ((size_t)(L - 1) * BLOCK + tid) * KG, &pcn[0][0]);
+    double Nn = ns[(L - 1) * SPB + q];
+    for (long long t = L - 1; t >= 0; --t) {
+      MT lcur[G][K];
+      float pcur[G][K];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) { lcur[g][a] = lcn[g][a]; pcur[g][a] = pcn[g][a]; }
+      const double Nt = Nn;
+      if (t > 0) {
+        load_vec<KG>(hl + ((size_t)(t - 1) * BLOCK + tid) * KG, &lcn[0][0]);
+        load_vec<KG>(hp + ((size_t)(t - 1) * BLOCK + tid) * KG, &pcn[0][0]);
+        Nn = ns[(t - 1) * SPB + q];
+      }
+      const float u = k.sc * wb[t];
+      const float gt = gb[t];
+      const float gtp = gt * k.csc;
+      const float gwh = gt * whb[t];
+      const MT LZ = (MT)((lz2 - Nt) - Np);
+      float qrc[G][K];  // Psi_t - g_t w_hat_t at the row offsets
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) qrc[g][r] = qr[g][r] - gwh;
+      float gw = 0.f;
+      MT mx = (MT)-INFINITY;
+      MT rout[G][K];
+      float qout[G][K];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          MT y[K];
+          float dd[K];
+          MT m = (MT)-INFINITY;
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            dd[r] = u - V[g][r][a];
+            y[r] = emit<P>(u, V[g][r][a], rr[g][r], k.kap);
+            m = tmax(m, y[r]);
+          }
+          float e[K], t2[K];
+          float cs = 0.f, ps = 0.f;
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            e[r] = ex2((float)(y[r] - m));
+            cs += e[r];
+            t2[r] = __builtin_fmaf(gtp, V[g][r][a], qrc[g][r]);
+            ps = __builtin_fmaf(e[r], t2[r], ps);
+          }
+          rout[g][a] = m + (MT)lg2(cs);
+          qout[g][a] = ps * rcp_nr(cs);
+          mx = tmax(mx, rout[g][a]);
+          const float f = ex2((float)((m + lcur[g][a]) - LZ));
+          const float pa = pcur[g][a] + h;
+          if (valid) {
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              const float gm = e[r] * f;
+              const float eh = gm * (t2[r] + pa);
+              gw = __builtin_fmaf(V[g][r][a], eh, gw);
+              acc[g][r][a] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, acc[g][r][a]));
+            }
+          }
+        }
+      MT* mw = msgl[mb] + q * M;
+      float* pw = msgp[mb] + q * M;
+      if (t > 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            mw[p + g * LPS + a * NG] = rout[g][a];
+            pw[p + g * LPS + a * NG] = qout[g][a];
+          }
+      }
+      MT v2[2] = {(MT)gw, mx};
+      chain_reduce<C, 2, 2u>(v2, red, rp);
+      if (valid && p == 0)
+        grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+      if (t == 0) break;
+      const MT sh = floor(v2[1]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        MT tm[K];
+        float tp[K];
+        load_vec<K>(mw + K * (p + g * LPS), tm);
+        load_vec<K>(pw + K * (p + g * LPS), tp);
+#pragma unroll
+        for (int r = 0; r < K; ++r) { rr[g][r] = tm[r] - sh; qr[g][r] = tp[r]; }
+      }
+      Np += (double)sh;
+      if constexpr (C::DB) mb ^= 1; else __syncthreads();
+    }
+  }
+
+  // Codebook-gradient partial of this slot: combine the chains of the block (fixed xor order),
+  // then one copy writes its states.
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int r = 0; r < K; ++r)
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        float v = acc[g][r][a];
+        if constexpr (SPB > 1) {
+#pragma unroll
+          for (int o = LPS; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+        }
+        if (q == 0) partial[(size_t)blockIdx.x * C::S + K * (p + g * LPS) + r + a * M] = v;
+      }
+}
+
+// out[s] = sum over slots of the partials, in slot order (deterministic); with no slots, 0.
+__global__ void __launch_bounds__(256)
+k_reduce_slots(const float* __restrict__ partial, long long slots, long long count,
+               float* __restrict__ out) {
+  const long long s = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (s >= count) return;
+  float acc = 0.f;
+  for (long long i = 0; i < slots; ++i) acc += partial[(size_t)i * count + s];
+  out[s] = acc;
+}
+
+// Messages are carried in fp64 below this temperature, for every shape whose backward
+// message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS.
+constexpr float kPreciseBelowT = 0.05f;
+template <int n, int k>
+constexpr bool precise_fits() {
+  return (long long)geom_spb(n, k) * ((1LL << n) >> k) * 12 <= 150 * 1024;
+}
+template <int n, int k>
+bool use_precise(float T) {
+  return precise_fits<n, k>() && T < kPreciseBelowT;
+}
+
+Consts make_consts(float T, bool precise) {
+  Consts c;
+  const double kap = kLog2e / (double)T;
+  c.kap = kap;
+  c.inv_t = 1.0f / T;
+  if (precise) {
+    c.sc = 1.0f;
+    c.csc = 1.0f;
+  } else {
+    c.sc = (float)sqrt(kap);
+    c.csc = 1.0f / c.sc;
+  }
+  return c;
+}
+
+template <int n, int k, class P>
+int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
+              float T, float* w_hat, float* log_z, float* saved, void* ws, hipStream_t st) {
+  using C = Cfg<(1 << k), geom_g(n, k), geom_lps(n, k), P, false>;
+  static_assert(C::S == (1 << n), "geometry mismatch");
+  const Consts kc = make_consts(T, P::kPrecise);
+  const size_t slot = sparse_fwd_slot_bytes(g, L);
+  double* slz = reinterpret_cast<double*>(saved);
+  float* swh = saved + saved_what_offset(B);
+  hipLaunchKernelGGL((k_sparse_fwd<C>), dim3((unsigned)g.slots), dim3(C::BLOCK), 0, st, cb, w, B, L,
+                     kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units);
+  return (int)hipGetLastError();
+}
+
+template <int n, int k, class P>
+int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
+              float T, const float* saved, const float* gup, const float* hup, float* grad_w,
+              float* grad_c, void* ws, hipStream_t st) {
+  using C = Cfg<(1 << k), geom_g(n, k), geom_lps(n, k), P, true>;
+  static_assert(C::S == (1 << n), "geometry mismatch");
+  const Consts kc = make_consts(T, P::kPrecise);
+  const size_t slot = sparse_bwd_slot_bytes(g, L);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + slot * (size_t)g.slots);
+  const double* slz = reinterpret_cast<const double*>(saved);
+  const float* swh = saved + saved_what_offset(B);
+  hipLaunchKernelGGL((k_sparse_bwd<C>), dim3((unsigned)g.slots), dim3(C::BLOCK), 0, st, cb, w, B, L,
+                     kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((C::S + 255) / 256)), dim3(256), 0, st, partial,
+                     (long long)g.slots, (long long)C::S, grad_c);
+  return (int)hipGetLastError();
+}
+
+template <int n, int k>
+int run_fwd(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
+            float T, float* w_hat, float* log_z, float* saved, void* ws, hipStream_t st) {
+  if constexpr (precise_fits<n, k>())
+    if (use_precise<n, k>(T))
+      return run_fwd_p<n, k, Precise>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, st);
+  return run_fwd_p<n, k, Fast>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, st);
+}
+
+template <int n, int k>
+int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
+            float T, const float* saved, const float* gup, const float* hup, float* grad_w,
+            float* grad_c, void* ws, hipStream_t st) {
+  if constexpr (precise_fits<n, k>())
+    if (use_precise<n, k>(T))
+      return run_bwd_p<n, k, Precise>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, st);
+  return run_bwd_p<n, k, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, st);
+}
+
+}  // namespace
+
+// Instantiated shapes: see geom_supported().
+#define BCJR_SPARSE_SHAPES(X) \
+  X(4, 2) X(5, 2) X(6, 2) X(7, 2) X(8, 2) X(9, 2) X(10, 2) X(11, 2) X(12, 2) X(13, 2) X(14, 2) \
+  X(15, 2) X(16, 2)
+
+int launch_sparse_forward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
+                          int64_t L, float T, float* w_hat, float* log_z, float* saved, void* ws,
+                          void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define X(N_, K_) \
+  if (g.n == N_ && g.k == K_) return run_fwd<N_, K_>(g, codebook, w, B, L, T, w_hat, log_z, saved, ws, st);
+  BCJR_SPARSE_SHAPES(X)
+#undef X
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_sparse_backward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
+                           int64_t L, float T, const float* saved, const float* grad_w_hat,
+                           const float* grad_log_z, float* grad_w, float* grad_codebook, void* ws,
+                           void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define X(N_, K_)                                                                          \
+  if (g.n == N_ && g.k == K_)                                                              \
+    return run_bwd<N_, K_>(g, codebook, w, B, L, T, saved, grad_w_hat, grad_log_z, grad_w, \
+                           grad_codebook, ws, st);
+  BCJR_SPARSE_SHAPES(X)
+#undef X
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_fill_zero(float* dst, int64_t count, void* stream) {
+  if (count <= 0) return 0;
+  hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), nullptr, 0LL, (long long)count, dst);
+  return (int)hipGetLastError();
+}
+
+bool sparse_shape_built(int n, int k) {
+#define X(N_, K_) if (n == N_ && k == K_) return true;
+  BCJR_SPARSE_SHAPES(X)
+#undef X
+  return false;
+}
+
+}  // namespace bcjr

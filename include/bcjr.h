@@ -1,0 +1,135 @@
+/*
+ * bcjr.h -- C ABI of the MI355X (gfx950) BCJR soft trellis decoder.
+ *
+ * Method: "BCJR-QAT: A Differentiable Relaxation of Trellis-Coded Weight Quantization"
+ * (V. Iyengar, arXiv 2605.10655). The paper's abstract (gptget.net/papers/2605.10655,
+ * "Abstract") replaces the non-differentiable Viterbi argmax of trellis-coded weight
+ * quantisation by the BCJR forward-backward sum-product recursion at temperature T; the soft
+ * codeword is the Boltzmann expectation over trellis paths, exactly differentiable, equal to
+ * the hard code as T -> 0, and computed like the transfer matrix of a 1D Ising-like chain.
+ * The gist.science technical summary ("Core mechanism") writes the soft codeword as
+ *   w_hat_t(T) = <c(s_t)>_{p_T} = sum_s c(s) p_T(s_t = s | w),
+ * and ("Key technical innovations") states that the O(L*S^2) forward-backward gives exact
+ * gradients through the trellis, fused into one launch at fp32 parity.
+ *
+ * Readings used where the pages are silent (the pages give neither the energy nor the
+ * trellis shape):
+ *   - path energy E = sum_t (w_t - c(s_t))^2, path weight exp(-E/T), natural-log log Z;
+ *   - bitshift trellis: S = 2^n states, K = 2^k branches, s' = ((s << k) | b) & (S - 1),
+ *     free start and free end state, one weight per step;
+ *   - dense trellis: every state may follow every state; theta(s, s') is a transition
+ *     log-potential that enters the energy as -theta, so the edge weight is exp(theta/T).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked DEVICE are device (HBM) pointers; arrays are row-major, contiguous,
+ *     fp32 unless stated. "B, L" are the number of chains and the weights per chain.
+ *   - The caller owns every buffer. The library allocates no device memory and keeps no
+ *     mutable global state. Workspaces (ws) must be 16-byte aligned (BCJR_E_WORKSPACE
+ *     otherwise); their contents on entry are irrelevant and on return unspecified.
+ *   - All arguments are validated on the host before anything is enqueued. On any error
+ *     nothing is enqueued and no output buffer is touched.
+ *   - Calls are asynchronous on the given stream (NULL = the default stream) and never
+ *     synchronise. A launch failure is reported as BCJR_E_DEVICE by the call that sees it.
+ *   - NaN or Inf in w, the codebook or theta propagate to the outputs unchecked.
+ *   - Results are bitwise deterministic for a given device, input and argument set.
+ *   - The library is thread safe (no shared mutable state); use one stream per thread.
+ */
+#ifndef BCJR_H_
+#define BCJR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* bcjr_stream_t; /* a hipStream_t */
+
+typedef enum {
+  BCJR_OK = 0,
+  BCJR_E_ARG = 1,         /* null required pointer, T <= 0 or not finite, bad flag        */
+  BCJR_E_SHAPE = 2,       /* n outside [1,16], k outside [1,n], B < 0, L < 1, S mismatch   */
+  BCJR_E_WORKSPACE = 3,   /* ws_bytes smaller than the matching *_workspace_bytes query    */
+  BCJR_E_DEVICE = 4,      /* a HIP call or kernel launch failed                            */
+  BCJR_E_UNSUPPORTED = 5  /* valid shape with no kernel built for it (see bcjr_supported)  */
+} bcjr_status;
+
+/* Bitshift trellis (the pages do not give the trellis shape; this is the reading above). */
+typedef struct {
+  int32_t state_bits;       /* n in [1,16]; S = 1 << n states                              */
+  int32_t bits_per_step;    /* k in [1,n];  K = 1 << k; successor s' = ((s<<k)|b) & (S-1)  */
+  int32_t weights_per_step; /* V; must be 1 (else BCJR_E_UNSUPPORTED)                      */
+  const float* codebook;    /* DEVICE [S]: codeword c(s) emitted in state s                 */
+} bcjr_trellis;
+
+/* Query: 1 if a kernel exists for this (n, k, V), else 0. Host only. */
+int bcjr_supported(const bcjr_trellis* tr);
+
+/* Bytes of the forward -> backward context: the forward's per-chain log2 Z (as an exact
+ * integer part and a fraction, fp32 [B][2]), which
+ * the backward uses to normalise the posteriors, and its soft codeword (fp32 [B,L]), on which
+ * the backward centres its conditional expectations. Returns 0 for an invalid shape. Host
+ * only, needs no device. */
+size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L);
+
+/* Bytes of device workspace for a call: which = 0 forward, 1 backward, 2 viterbi.
+ * Returns 0 for an invalid shape or flag. Host only, needs no device. The workspace holds
+ * per-slot message histories (the alpha-side messages of one sweep, read back by the
+ * sweep in the other direction) and, for the backward, per-slot codebook-gradient partials. */
+size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int which);
+
+/*
+ * Forward: soft codeword and log partition function of every chain.
+ *   w_hat[b,t] = sum_s c(s) p_T(s_t = s | w_b)      (technical summary, "Core mechanism")
+ *   log_z[b]   = log sum_paths exp(-E(path)/T)      (abstract: Boltzmann distribution over
+ *                                                     trellis paths, transfer-matrix form)
+ * w      DEVICE [B,L]  weight preimage, read only
+ * T      temperature, finite and > 0
+ * w_hat  DEVICE [B,L]  written
+ * log_z  DEVICE [B]    written
+ * saved  DEVICE, bcjr_saved_bytes() bytes, written; pass it unchanged to bcjr_backward
+ * ws     DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 0); contents are scratch
+ * B = 0 is valid and enqueues nothing.
+ */
+bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
+                         float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,
+                         bcjr_stream_t stream);
+
+/*
+ * Backward: exact reverse-mode gradient of  F = sum_{b,t} g[b,t] w_hat[b,t] + sum_b h[b] log_z[b]
+ * ("exactly differentiable", abstract; "exact gradients", technical summary, "Key technical
+ * innovations") with respect to the weights and the codebook. T is not differentiated.
+ * w, T, tr   exactly as given to the forward that wrote `saved`
+ * saved      DEVICE, read only
+ * grad_w_hat DEVICE [B,L] upstream gradient g
+ * grad_log_z DEVICE [B] upstream gradient h, or NULL for h = 0
+ * grad_w     DEVICE [B,L] written
+ * grad_codebook DEVICE [S] written (overwritten, summed over all B chains, fixed-order sum)
+ * ws         DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 1)
+ */
+bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
+                          const void* saved, const float* grad_w_hat, const float* grad_log_z,
+                          float* grad_w, float* grad_codebook, void* ws, size_t ws_bytes,
+                          bcjr_stream_t stream);
+
+/*
+ * Viterbi decode, the T -> 0 limit ("recovering the hard QTIP code as T -> 0", abstract).
+ * fp32 min-sum with a fixed op order: e = fl(d*d), d = fl(w_t - c(s)); m_1 = e_1;
+ * m_t(s') = fl(min_a m_{t-1}(p_a(s')) + e_t(s')) where p_a(s') = (s' >> k) | (a << (n-k)) and
+ * the lowest a wins an exact tie; the final state is the lowest index attaining min m_L.
+ * states DEVICE int32 [B,L] written: the decoded state path
+ * w_hard DEVICE [B,L] written with c(states), or NULL
+ * ws     DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 2) (backpointers)
+ */
+bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                           int32_t* states, float* w_hard, void* ws, size_t ws_bytes,
+                           bcjr_stream_t stream);
+
+/* Text of a status code (static storage). */
+const char* bcjr_status_string(bcjr_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BCJR_H_ */

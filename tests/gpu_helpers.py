@@ -1,0 +1,59 @@
+"""Shared helpers of the GPU parity tests (tolerances, case logging, device runs)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from bcjr_soft_decoding_amd import bcjr
+
+# Tolerances stated for the path: rel 1e-4 on the soft codeword and log Z, rel 1e-3 on the
+# gradients, in fp32 against the fp64 oracle. Arrays with entries near zero are compared
+# normwise per element: |x - ref| <= rtol * max(|ref|, rms(ref)).
+RTOL_FWD = 1e-4
+RTOL_GRAD = 1e-3
+
+
+def log_case(msg: str):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def assert_normwise(x, ref, rtol, what=""):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (what, x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), f"{what}: non-finite values"
+    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref * ref)))
+    err = np.abs(x - ref) / scale
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= rtol, f"{what}: worst normwise error {worst:.3e} > {rtol:.1e}"
+    return worst
+
+
+def assert_rel(x, ref, rtol, what=""):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(x - ref) / np.maximum(np.abs(ref), 1e-30)
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= rtol, f"{what}: worst relative error {worst:.3e} > {rtol:.1e}"
+    return worst
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_fwd_bwd(n, k, c, w, T, g=None, h=None):
+    """One forward (+ backward if g is given) through the C ABI; returns numpy results."""
+    cd, wd = dev(c), dev(w)
+    w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, k, T)
+    out = {"w_hat": w_hat, "log_z": log_z}
+    if g is not None:
+        gd = dev(g)
+        hd = None if h is None else dev(h)
+        gw, gc = bcjr.bcjr_backward(cd, wd, n, k, T, saved, gd, hd)
+        out.update(grad_w=gw, grad_codebook=gc)
+    torch.cuda.synchronize()
+    return {key: v.cpu().numpy() for key, v in out.items()}

@@ -1,0 +1,179 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bcjr_soft_decoding_amd import bcjr, synth
+from tests.gpu_helpers import (RTOL_FWD, RTOL_GRAD, assert_normwise, assert_rel, dev, log_case,
+                               run_fwd_bwd)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bcjr.lib()  # raises if the HIP library is missing: no fallback
+
+
+def _compare(n, k, c, w, T, g=None, h=None, tag=""):
+    log_case(f"{tag} n={n} k={k} B={w.shape[0]} L={w.shape[1]} T={T} grad={g is not None}")
+    got = run_fwd_bwd(n, k, c, w, T, g, h)
+    ref = oracle.sparse_forward(n, k, c, w, T)
+    assert_normwise(got["w_hat"], ref["w_hat"], RTOL_FWD, f"{tag} w_hat")
+    assert_rel(got["log_z"], ref["log_z"], RTOL_FWD, f"{tag} log_z")
+    if g is not None:
+        rb = oracle.sparse_backward(n, k, c, w, T, g, h)
+        assert_normwise(got["grad_w"], rb["grad_w"], RTOL_GRAD, f"{tag} grad_w")
+        assert_normwise(got["grad_codebook"], rb["grad_codebook"], RTOL_GRAD, f"{tag} grad_c")
+    return got
+
+
+# ------------------------------------------------------------------------------------------
+# Workload 1: S=16, k=2, 8 x 64, three temperatures, fwd + bwd, plus Viterbi
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T", synth.WORKLOADS[1].temps)
+def test_workload1_fwd_bwd(T):
+    c, w, g = synth.codebook(1), synth.weights(1), synth.upstream_grad(1)
+    _compare(4, 2, c, w, T, g, None, "wl1")
+    _compare(4, 2, c, w, T, g, synth.logz_grad(1), "wl1+h")
+
+
+def test_workload1_viterbi_bit_exact():
+    c, w = synth.codebook(1), synth.weights(1)
+    log_case("wl1 viterbi")
+    st, wh = bcjr.viterbi_decode(dev(c), dev(w), 4, 2)
+    ref = oracle.viterbi(4, 2, c, w)
+    np.testing.assert_array_equal(st.cpu().numpy(), ref["states"])
+    np.testing.assert_array_equal(wh.cpu().numpy(), ref["w_hard"])
+
+
+# ------------------------------------------------------------------------------------------
+# Workload 2: S=256, k=2; a ragged prefix of the chains (509 = 4*127 + 1 chains per block of 4)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T", synth.WORKLOADS[2].temps)
+def test_workload2_fwd_bwd_prefix(T):
+    c = synth.codebook(2)
+    w = synth.weights(2)[:509]
+    g = synth.upstream_grad(2)[:509]
+    _compare(8, 2, c, w, T, g, None, "wl2")
+
+
+def test_workload2_viterbi_bit_exact_full():
+    c, w = synth.codebook(2), synth.weights(2)
+    log_case("wl2 viterbi full 4096x256")
+    st, wh = bcjr.viterbi_decode(dev(c), dev(w), 8, 2)
+    ref = oracle.viterbi(8, 2, c, w)
+    np.testing.assert_array_equal(st.cpu().numpy(), ref["states"])
+    np.testing.assert_array_equal(wh.cpu().numpy(), ref["w_hard"])
+
+
+# ------------------------------------------------------------------------------------------
+# Every built state size, small random chains (covers every kernel instantiation)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n", list(range(4, 17)))
+def test_all_state_sizes(n):
+    B = 3 if n < 15 else 2
+    L = 13
+    c = synth.normal(300 + n, (1 << n,))
+    w = synth.normal(400 + n, (B, L))
+    g = synth.normal(500 + n, (B, L))
+    h = synth.normal(600 + n, (B,))
+    _compare(n, 2, c, w, 0.3, g, h, "sizes")
+    log_case(f"sizes viterbi n={n}")
+    st, _ = bcjr.viterbi_decode(dev(c), dev(w), n, 2)
+    np.testing.assert_array_equal(st.cpu().numpy(), oracle.viterbi(n, 2, c, w)["states"])
+
+
+# ------------------------------------------------------------------------------------------
+# Edge cases
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n,B,L", [(8, 1, 1), (8, 5, 1), (12, 1, 2), (4, 65, 3), (6, 17, 31),
+                                   (10, 2, 129), (12, 3, 1)])
+def test_edge_shapes(n, B, L):
+    c = synth.normal(700 + n, (1 << n,))
+    w = synth.normal(800 + n + L, (B, L))
+    g = synth.normal(900 + n + L, (B, L))
+    _compare(n, 2, c, w, 0.2, g, None, "edge")
+
+
+def test_zero_chains_is_a_no_op():
+    c = dev(synth.codebook(2))
+    w = torch.empty((0, 16), dtype=torch.float32, device="cuda")
+    log_case("B=0")
+    w_hat, log_z, saved = bcjr.bcjr_forward(c, w, 8, 2, 0.5)
+    gw, gc = bcjr.bcjr_backward(c, w, 8, 2, 0.5, saved, torch.empty_like(w))
+    torch.cuda.synchronize()
+    assert w_hat.numel() == 0 and torch.count_nonzero(gc).item() == 0
+
+
+def test_extreme_temperatures():
+    """Very low and very high T stay finite and match the oracle."""
+    c = synth.normal(1201, (256,))
+    w = synth.normal(1202, (16, 64))
+    g = synth.normal(1203, (16, 64))
+    for T in (0.003, 50.0):
+        _compare(8, 2, c, w, T, g, None, "extremeT")
+
+
+# ------------------------------------------------------------------------------------------
+# Full-size workloads in the benchmark's launch configuration, sampled chains vs the oracle
+# ------------------------------------------------------------------------------------------
+def _full_size(i, T, sample):
+    wl = synth.WORKLOADS[i]
+    c, w, g = synth.codebook(i), synth.weights(i), synth.upstream_grad(i)
+    log_case(f"full workload {i} ({wl.name}) B={wl.B} L={wl.L} S={wl.S} T={T}")
+    got = run_fwd_bwd(wl.n, wl.k, c, w, T, g)
+    for arr in got.values():
+        assert np.all(np.isfinite(arr))
+    ref = oracle.sparse_forward(wl.n, wl.k, c, w[sample], T)
+    rb = oracle.sparse_backward(wl.n, wl.k, c, w[sample], T, g[sample])
+    assert_normwise(got["w_hat"][sample], ref["w_hat"], RTOL_FWD, "w_hat (sampled)")
+    assert_rel(got["log_z"][sample], ref["log_z"], RTOL_FWD, "log_z (sampled)")
+    assert_normwise(got["grad_w"][sample], rb["grad_w"], RTOL_GRAD, "grad_w (sampled)")
+    # the codebook gradient sums over all chains: check the exact translation identity
+    #   sum_t,b grad_w + sum_s grad_c = sum_t,b g
+    lhs = got["grad_w"].astype(np.float64).sum() + got["grad_codebook"].astype(np.float64).sum()
+    rhs = g.astype(np.float64).sum()
+    scale = np.abs(got["grad_w"]).astype(np.float64).sum() + np.abs(got["grad_codebook"]).sum()
+    assert abs(lhs - rhs) <= 1e-4 * scale, (lhs, rhs, scale)
+
+
+def test_workload3_llama_mlp_full_size_sampled():
+    _full_size(3, 0.1, [0, 1, 4097, 33333, 65535])
+
+
+@pytest.mark.parametrize("T", synth.WORKLOADS[4].temps)
+def test_workload4_s65536_full_size_sampled(T):
+    _full_size(4, T, [0, 16383])
+
+
+def test_workload3_codebook_gradient_on_a_prefix():
+    c = synth.codebook(3)
+    w = synth.weights(3)[:96]
+    g = synth.upstream_grad(3)[:96]
+    _compare(12, 2, c, w, 0.1, g, None, "wl3 prefix")
+
+
+# ------------------------------------------------------------------------------------------
+# Determinism and workspace hygiene
+# ------------------------------------------------------------------------------------------
+def test_bitwise_deterministic_and_poisoned_workspace():
+    n, k, T = 12, 2, 0.1
+    c, w, g = dev(synth.codebook(3)), dev(synth.weights(3)[:700]), dev(synth.upstream_grad(3)[:700])
+    B, L = w.shape
+    log_case("determinism")
+    outs = []
+    for poison in (0.0, float("nan")):
+        wsf = bcjr.workspace(n, k, B, L, bcjr.FWD)
+        wsb = bcjr.workspace(n, k, B, L, bcjr.BWD)
+        wsf.view(torch.uint8).fill_(0xFF if poison != 0.0 else 0)  # 0xFFFFFFFF is a NaN
+        wsb.view(torch.uint8).fill_(0xFF if poison != 0.0 else 0)
+        wh, lz, sv = bcjr.bcjr_forward(c, w, n, k, T, ws=wsf)
+        gw, gc = bcjr.bcjr_backward(c, w, n, k, T, sv, g, ws=wsb)
+        torch.cuda.synchronize()
+        outs.append([x.cpu().numpy().copy() for x in (wh, lz, gw, gc)])
+    for a, b in zip(*outs):
+        assert np.all(np.isfinite(a))
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
