@@ -12,7 +12,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libbcjr.so")
+# BCJR_LIB may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("BCJR_LIB", os.path.join(_PKG, "_lib", "libbcjr.so"))
 
 BCJR_OK, BCJR_E_ARG, BCJR_E_SHAPE, BCJR_E_WORKSPACE, BCJR_E_DEVICE, BCJR_E_UNSUPPORTED = range(6)
 FWD, BWD, VIT = 0, 1, 2

@@ -13,7 +13,13 @@
 
 namespace bcjr {
 
+enum Kind { kFwd = 0, kBwd = 1, kVit = 2 };
+
 constexpr int kMaxLanesPerChain = 1024;
+
+// States per lane each kernel aims for (more states per lane: fewer lanes per chain, cheaper
+// per-step exchanges and reductions, more registers). Measured on MI355X at S = 4096.
+constexpr int geom_target_states(int kind) { return kind == kFwd ? 64 : kind == kBwd ? 32 : 16; }
 
 // Kernels are built for k in {1, 2, 3} and 2k <= n <= 16, except where the two backward
 // messages of one chain (2 * S/K floats, single-buffered) would not fit the 160 KiB of LDS.
@@ -21,15 +27,31 @@ constexpr bool geom_supported(int n, int k) {
   return k >= 1 && k <= 3 && n >= 2 * k && n <= 16 && 2LL * ((1LL << n) >> k) * 4 <= 160 * 1024;
 }
 constexpr int geom_ng(int n, int k) { return 1 << (n - 2 * k); }
-constexpr int geom_lps(int n, int k) {
-  return geom_ng(n, k) < kMaxLanesPerChain ? geom_ng(n, k) : kMaxLanesPerChain;
+constexpr int geom_cmin(int a, int b) { return a < b ? a : b; }
+constexpr int geom_cmax(int a, int b) { return a > b ? a : b; }
+// blocks per lane: the target (at least 1, at most NG), raised if needed to keep LPS <= 1024
+constexpr int geom_g(int n, int k, int kind) {
+  return geom_cmax(geom_cmin(geom_cmax(geom_target_states(kind) >> (2 * k), 1), geom_ng(n, k)),
+                   geom_ng(n, k) / kMaxLanesPerChain);
 }
-constexpr int geom_g(int n, int k) { return geom_ng(n, k) / geom_lps(n, k); }
-constexpr int geom_spb(int n, int k) { return geom_lps(n, k) < 64 ? 64 / geom_lps(n, k) : 1; }
-constexpr int geom_block(int n, int k) { return geom_lps(n, k) < 64 ? 64 : geom_lps(n, k); }
-// Blocks are persistent: each loops over chain units; about 16 waves per CU on 256 CUs.
-constexpr long long geom_max_slots(int n, int k) {
-  return (256LL * 16 * 64) / geom_block(n, k);
+constexpr int geom_lps(int n, int k, int kind) { return geom_ng(n, k) / geom_g(n, k, kind); }
+constexpr int geom_spb(int n, int k, int kind) {
+  return geom_lps(n, k, kind) < 64 ? 64 / geom_lps(n, k, kind) : 1;
 }
+constexpr int geom_block(int n, int k, int kind) {
+  return geom_lps(n, k, kind) < 64 ? 64 : geom_lps(n, k, kind);
+}
+// Blocks are persistent: each loops over chain units. Workspace slots cover the largest
+// resident grid on a 256-CU device at 8 waves per SIMD (32 per CU); a launch uses
+// min(slots, resident blocks) of them.
+constexpr long long geom_max_slots(int n, int k, int kind) {
+  return (256LL * 32 * 64) / geom_block(n, k, kind);
+}
+
+static_assert(geom_g(12, 2, kFwd) == 4 && geom_lps(12, 2, kFwd) == 64, "S=4096 forward geometry");
+static_assert(geom_g(12, 2, kBwd) == 2 && geom_lps(12, 2, kBwd) == 128, "S=4096 backward geometry");
+static_assert(geom_g(16, 2, kBwd) == 4 && geom_lps(16, 2, kBwd) == 1024, "S=65536 geometry");
+static_assert(geom_g(4, 2, kFwd) == 1 && geom_lps(4, 2, kFwd) == 1, "S=16 geometry");
+static_assert(geom_g(8, 2, kBwd) == 2 && geom_lps(8, 2, kBwd) == 8, "S=256 geometry");
 
 }  // namespace bcjr

@@ -10,7 +10,7 @@
 
 namespace bcjr {
 
-bool sparse_geom(int n, int k, int64_t B, SparseGeom* g) {
+bool sparse_geom(int n, int k, int64_t B, int kind, SparseGeom* g) {
   if (!geom_supported(n, k) || !sparse_shape_built(n, k)) return false;
   g->n = n;
   g->k = k;
@@ -18,14 +18,26 @@ bool sparse_geom(int n, int k, int64_t B, SparseGeom* g) {
   g->S = 1 << n;
   g->M = g->S / g->K;
   g->NG = geom_ng(n, k);
-  g->G = geom_g(n, k);
-  g->LPS = geom_lps(n, k);
-  g->SPB = geom_spb(n, k);
-  g->BLOCK = geom_block(n, k);
+  g->G = geom_g(n, k, kind);
+  g->LPS = geom_lps(n, k, kind);
+  g->SPB = geom_spb(n, k, kind);
+  g->BLOCK = geom_block(n, k, kind);
   g->units = B > 0 ? (B + g->SPB - 1) / g->SPB : 0;
-  const int64_t mx = geom_max_slots(n, k);
+  const int64_t mx = geom_max_slots(n, k, kind);
   g->slots = g->units < mx ? g->units : mx;
   return true;
+}
+
+// Persistent grid: every block must be resident at once (each loops over its chain units),
+// so the grid is the smaller of the workspace slots and the device's resident capacity for
+// this kernel (occupancy x compute units).
+int resident_grid(const void* kernel, int block, int64_t slots) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return -1;
+  const int64_t cap = (int64_t)(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  return (int)(slots < cap ? slots : cap);
 }
 
 size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L) {
@@ -50,11 +62,11 @@ bool shape_ok(const bcjr_trellis* tr) {
 }
 
 // Common validation. On success fills *g (for B > 0) and returns BCJR_OK.
-bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, SparseGeom* g) {
+bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, int kind, SparseGeom* g) {
   if (tr == nullptr) return BCJR_E_ARG;
   if (!shape_ok(tr) || B < 0 || L < 1) return BCJR_E_SHAPE;
   if (tr->weights_per_step != 1) return BCJR_E_UNSUPPORTED;
-  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, g)) return BCJR_E_UNSUPPORTED;
+  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, kind, g)) return BCJR_E_UNSUPPORTED;
   if (B > 0 && tr->codebook == nullptr) return BCJR_E_ARG;
   return BCJR_OK;
 }
@@ -75,7 +87,7 @@ extern "C" {
 int bcjr_supported(const bcjr_trellis* tr) {
   if (tr == nullptr || !shape_ok(tr) || tr->weights_per_step != 1) return 0;
   SparseGeom g;
-  return sparse_geom(tr->state_bits, tr->bits_per_step, 1, &g) ? 1 : 0;
+  return sparse_geom(tr->state_bits, tr->bits_per_step, 1, kFwd, &g) ? 1 : 0;
 }
 
 size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L) {
@@ -85,8 +97,9 @@ size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L) {
 
 size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int which) {
   if (tr == nullptr || !shape_ok(tr) || B < 0 || L < 1 || tr->weights_per_step != 1) return 0;
+  if (which < 0 || which > 2) return 0;
   SparseGeom g;
-  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, &g)) return 0;
+  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, which, &g)) return 0;
   if (B == 0) return 0;
   switch (which) {
     case 0: return sparse_fwd_ws_bytes(g, L);
@@ -100,7 +113,7 @@ bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int6
                          float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,
                          bcjr_stream_t stream) {
   SparseGeom g;
-  bcjr_status st = check_common(tr, B, L, &g);
+  bcjr_status st = check_common(tr, B, L, kFwd, &g);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
   if (B == 0) return BCJR_OK;
@@ -116,7 +129,7 @@ bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int
                           float* grad_w, float* grad_codebook, void* ws, size_t ws_bytes,
                           bcjr_stream_t stream) {
   SparseGeom g;
-  bcjr_status st = check_common(tr, B, L, &g);
+  bcjr_status st = check_common(tr, B, L, kBwd, &g);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
   if (grad_codebook == nullptr) return BCJR_E_ARG;
@@ -136,7 +149,7 @@ bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, in
                            int32_t* states, float* w_hard, void* ws, size_t ws_bytes,
                            bcjr_stream_t stream) {
   SparseGeom g;
-  bcjr_status st = check_common(tr, B, L, &g);
+  bcjr_status st = check_common(tr, B, L, kVit, &g);
   if (st != BCJR_OK) return st;
   if (B == 0) return BCJR_OK;
   if (!w || !states) return BCJR_E_ARG;

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "bcjr.h"
+#include "geom.h"
 
 namespace bcjr {
 
@@ -21,14 +22,14 @@ struct SparseGeom {
   int SPB;       // chains per block (LPS < 64: 64 / LPS, else 1)
   int BLOCK;     // threads per block
   int64_t units; // ceil(B / SPB)
-  int64_t slots; // blocks launched (= workspace slots)
+  int64_t slots; // workspace slots = the most blocks a launch may use
 };
 
 // True if kernels for (n, k) are compiled into the library (sparse_kernels.hip).
 bool sparse_shape_built(int n, int k);
 
 // Returns false if no kernel is built for (n, k).
-bool sparse_geom(int n, int k, int64_t B, SparseGeom* g);
+bool sparse_geom(int n, int k, int64_t B, int kind, SparseGeom* g);
 
 // Layout of the forward -> backward context: log2 Z of every chain as a double [B] (padded to
 // a multiple of 32 doubles), then the soft codeword w_hat [B, L] in fp32.
@@ -64,6 +65,8 @@ int launch_sparse_backward(const SparseGeom& g, const float* codebook, const flo
                            const float* grad_log_z, float* grad_w, float* grad_codebook, void* ws,
                            void* stream);
 int launch_fill_zero(float* dst, int64_t count, void* stream);
+// Grid of a persistent kernel: min(slots, resident blocks on the current device), or -1.
+int resident_grid(const void* kernel, int block, int64_t slots);
 int launch_viterbi(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                    int64_t L, int32_t* states, float* w_hard, void* ws, void* stream);
 

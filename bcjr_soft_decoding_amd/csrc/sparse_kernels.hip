@@ -86,8 +86,9 @@ __device__ __forceinline__ typename P::MT emit(float u, float v, typename P::MT 
     return __builtin_fmaf(-d, d, off);
   }
 }
-template <class T>
-__device__ __forceinline__ T tmax(T a, T b) { return a > b ? a : b; }
+// max through the hardware max instructions (v_max3_f32 / v_max_f64)
+__device__ __forceinline__ float tmax(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ double tmax(double a, double b) { return fmax(a, b); }
 
 template <int K_, int G_, int LPS_, class P_, bool BWD_>
 struct Cfg {
@@ -110,15 +111,33 @@ struct Cfg {
   static constexpr int NBUF = DB ? 2 : 1;
 };
 
-// Reduction over aligned groups of W lanes inside a wave (xor butterfly: every lane of the
-// group ends with the bitwise-identical result).
+// Cross-lane moves through DPP (no LDS round trip). CTRL: 0xB1 / 0x4E = quad_perm xor 1 / 2,
+// 0x141 = row_half_mirror (lane i <-> 7-i in each 8), 0x140 = row_mirror (i <-> 15-i).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffLL), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+template <class T>
+__device__ __forceinline__ T comb(T a, T b, bool is_max) { return is_max ? tmax(a, b) : a + b; }
+
+// Reduction over aligned groups of W lanes inside a wave. Every step combines two disjoint
+// halves symmetrically (a op b in one half, b op a in the other), so every lane of the group
+// ends with the bitwise-identical result.
 template <int W, class T>
 __device__ __forceinline__ T lanes_reduce(T v, bool is_max) {
-#pragma unroll
-  for (int o = W / 2; o >= 1; o >>= 1) {
-    const T o2 = __shfl_xor(v, o, 64);
-    v = is_max ? tmax(v, o2) : v + o2;
-  }
+  if constexpr (W >= 2) v = comb(v, dpp<0xB1>(v), is_max);
+  if constexpr (W >= 4) v = comb(v, dpp<0x4E>(v), is_max);
+  if constexpr (W >= 8) v = comb(v, dpp<0x141>(v), is_max);
+  if constexpr (W >= 16) v = comb(v, dpp<0x140>(v), is_max);
+  if constexpr (W >= 32) v = comb(v, __shfl_xor(v, 16, 64), is_max);
+  if constexpr (W >= 64) v = comb(v, __shfl_xor(v, 32, 64), is_max);
   return v;
 }
 
@@ -251,9 +270,9 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             x[a] = emit<P>(u, V[g][r][a], lc[g][a], k.kap);
             m = tmax(m, x[a]);
           }
-          float s = 0.f;
+          float s = ex2((float)(x[0] - m));
 #pragma unroll
-          for (int a = 0; a < K; ++a) s += ex2((float)(x[a] - m));
+          for (int a = 1; a < K; ++a) s += ex2((float)(x[a] - m));
           out[g][r] = m + (MT)lg2(s);
           mx = tmax(mx, out[g][r]);
         }
@@ -264,7 +283,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int r = 0; r < K; ++r) s2 += ex2((float)(out[g][r] - v1[0]));
+          for (int r = 0; r < K; ++r) s2 += ex2((float)(out[g][r] - v1[0]));  // once per chain
         float v2[1] = {s2};
         chain_reduce<C, 1, 0u>(v2, red, rp);
         lz2 = N + ((double)v1[0] + (double)lg2(v2[0]));
@@ -322,9 +341,10 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             y[r] = emit<P>(u, V[g][r][a], rr[g][r], k.kap);
             m = tmax(m, y[r]);
           }
-          float cs = 0.f, cw = 0.f;
+          float e0 = ex2((float)(y[0] - m));
+          float cs = e0, cw = V[g][0][a] * e0;
 #pragma unroll
-          for (int r = 0; r < K; ++r) {
+          for (int r = 1; r < K; ++r) {
             const float e = ex2((float)(y[r] - m));
             cs += e;
             cw = __builtin_fmaf(V[g][r][a], e, cw);
@@ -467,9 +487,10 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             x[a] = emit<P>(u, V[g][r][a], lc[g][a], k.kap);
             m = tmax(m, x[a]);
           }
-          float s = 0.f, ph = 0.f;
+          float e0 = ex2((float)(x[0] - m));
+          float s = e0, ph = e0 * __builtin_fmaf(gtp, V[g][r][0], pcc[g][0]);
 #pragma unroll
-          for (int a = 0; a < K; ++a) {
+          for (int a = 1; a < K; ++a) {
             const float e = ex2((float)(x[a] - m));
             s += e;
             ph = __builtin_fmaf(e, __builtin_fmaf(gtp, V[g][r][a], pcc[g][a]), ph);
@@ -554,12 +575,15 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             m = tmax(m, y[r]);
           }
           float e[K], t2[K];
-          float cs = 0.f, ps = 0.f;
 #pragma unroll
           for (int r = 0; r < K; ++r) {
             e[r] = ex2((float)(y[r] - m));
-            cs += e[r];
             t2[r] = __builtin_fmaf(gtp, V[g][r][a], qrc[g][r]);
+          }
+          float cs = e[0], ps = e[0] * t2[0];
+#pragma unroll
+          for (int r = 1; r < K; ++r) {
+            cs += e[r];
             ps = __builtin_fmaf(e[r], t2[r], ps);
           }
           rout[g][a] = m + (MT)lg2(cs);
@@ -641,7 +665,7 @@ k_reduce_slots(const float* __restrict__ partial, long long slots, long long cou
 constexpr float kPreciseBelowT = 0.05f;
 template <int n, int k>
 constexpr bool precise_fits() {
-  return (long long)geom_spb(n, k) * ((1LL << n) >> k) * 12 <= 150 * 1024;
+  return (long long)geom_spb(n, k, kBwd) * ((1LL << n) >> k) * 12 <= 150 * 1024;
 }
 template <int n, int k>
 bool use_precise(float T) {
@@ -666,13 +690,15 @@ Consts make_consts(float T, bool precise) {
 template <int n, int k, class P>
 int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, float* w_hat, float* log_z, float* saved, void* ws, hipStream_t st) {
-  using C = Cfg<(1 << k), geom_g(n, k), geom_lps(n, k), P, false>;
+  using C = Cfg<(1 << k), geom_g(n, k, kFwd), geom_lps(n, k, kFwd), P, false>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   const Consts kc = make_consts(T, P::kPrecise);
   const size_t slot = sparse_fwd_slot_bytes(g, L);
   double* slz = reinterpret_cast<double*>(saved);
   float* swh = saved + saved_what_offset(B);
-  hipLaunchKernelGGL((k_sparse_fwd<C>), dim3((unsigned)g.slots), dim3(C::BLOCK), 0, st, cb, w, B, L,
+  const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_fwd<C>), C::BLOCK, g.slots);
+  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_sparse_fwd<C>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w, B, L,
                      kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units);
   return (int)hipGetLastError();
 }
@@ -681,19 +707,21 @@ template <int n, int k, class P>
 int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, const float* saved, const float* gup, const float* hup, float* grad_w,
               float* grad_c, void* ws, hipStream_t st) {
-  using C = Cfg<(1 << k), geom_g(n, k), geom_lps(n, k), P, true>;
+  using C = Cfg<(1 << k), geom_g(n, k, kBwd), geom_lps(n, k, kBwd), P, true>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   const Consts kc = make_consts(T, P::kPrecise);
   const size_t slot = sparse_bwd_slot_bytes(g, L);
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + slot * (size_t)g.slots);
   const double* slz = reinterpret_cast<const double*>(saved);
   const float* swh = saved + saved_what_offset(B);
-  hipLaunchKernelGGL((k_sparse_bwd<C>), dim3((unsigned)g.slots), dim3(C::BLOCK), 0, st, cb, w, B, L,
+  const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_bwd<C>), C::BLOCK, g.slots);
+  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_sparse_bwd<C>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w, B, L,
                      kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((C::S + 255) / 256)), dim3(256), 0, st, partial,
-                     (long long)g.slots, (long long)C::S, grad_c);
+                     (long long)grid, (long long)C::S, grad_c);
   return (int)hipGetLastError();
 }
 

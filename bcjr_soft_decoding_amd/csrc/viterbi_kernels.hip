@@ -170,9 +170,11 @@ k_viterbi(const float* __restrict__ cb, const float* __restrict__ w, long long B
 template <int n, int k>
 int run_vit(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
             int32_t* states, float* w_hard, void* ws, hipStream_t st) {
-  using C = VCfg<(1 << k), geom_g(n, k), geom_lps(n, k)>;
+  using C = VCfg<(1 << k), geom_g(n, k, kVit), geom_lps(n, k, kVit)>;
   static_assert(C::S == (1 << n), "geometry mismatch");
-  hipLaunchKernelGGL((k_viterbi<C>), dim3((unsigned)g.slots), dim3(C::BLOCK), 0, st, cb, w, B, L,
+  const int grid = resident_grid(reinterpret_cast<const void*>(&k_viterbi<C>), C::BLOCK, g.slots);
+  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_viterbi<C>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w, B, L,
                      states, w_hard, static_cast<uint8_t*>(ws), (long long)g.units);
   return (int)hipGetLastError();
 }
