@@ -103,6 +103,8 @@ struct Cfg {
   static constexpr int SPB = LPS < 64 ? 64 / LPS : 1;
   static constexpr int BLOCK = LPS < 64 ? 64 : LPS;
   static constexpr int NWAVES = BLOCK / 64;
+  // stream the codebook from L2 when a 16-wave block leaves too few registers for it
+  static constexpr bool SV = LPS >= 1024 && G * K * K > 16;
   // LDS per buffer: the MT message (+ the fp32 expectation message in the backward).
   static constexpr long long BUF_BYTES = (long long)SPB * M * ((long long)sizeof(MT) + (BWD ? 4 : 0));
   // Double-buffer the message arrays when both buffers fit in 128 KiB, else one buffer and a
@@ -207,6 +209,51 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ src, T* dst) {
   }
 }
 
+// Per-lane codebook values v(s) = sc * c(s) of the lane's K x K blocks. Register-resident when
+// they fit; for chains of 1024 lanes (16-wave blocks, so at most 128 VGPRs per lane) they are
+// re-read from the L2-resident codebook one block at a time instead.
+template <class C, bool STREAM = C::SV>
+struct CodebookLane;
+template <class C>
+struct CodebookLane<C, false> {
+  float v[C::G][C::K][C::K];
+  __device__ __forceinline__ void init(const float* __restrict__ cb, float sc, int p) {
+#pragma unroll
+    for (int g = 0; g < C::G; ++g)
+#pragma unroll
+      for (int r = 0; r < C::K; ++r)
+#pragma unroll
+        for (int a = 0; a < C::K; ++a) v[g][r][a] = sc * cb[C::K * (p + g * C::LPS) + r + a * C::M];
+  }
+  __device__ __forceinline__ void get(int g, float (&out)[C::K][C::K]) const {
+#pragma unroll
+    for (int r = 0; r < C::K; ++r)
+#pragma unroll
+      for (int a = 0; a < C::K; ++a) out[r][a] = v[g][r][a];
+  }
+};
+template <class C>
+struct CodebookLane<C, true> {
+  const float* __restrict__ cb;
+  float sc;
+  int p;
+  __device__ __forceinline__ void init(const float* __restrict__ c, float s, int lane) {
+    cb = c;
+    sc = s;
+    p = lane;
+  }
+  __device__ __forceinline__ void get(int g, float (&out)[C::K][C::K]) const {
+    const float* base = cb + C::K * (p + g * C::LPS);
+#pragma unroll
+    for (int a = 0; a < C::K; ++a) {
+      float tmp[C::K];
+      load_vec<C::K>(base + a * C::M, tmp);
+#pragma unroll
+      for (int r = 0; r < C::K; ++r) out[r][a] = sc * tmp[r];
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------------------------
 // Forward: soft codeword and log Z.
 // ---------------------------------------------------------------------------------------------
@@ -227,13 +274,8 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
   const int q = LPS < 64 ? tid / LPS : 0;    // chain within the block
   const int p = LPS < 64 ? tid % LPS : tid;  // lane within the chain
 
-  float V[G][K][K];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int r = 0; r < K; ++r)
-#pragma unroll
-      for (int a = 0; a < K; ++a) V[g][r][a] = k.sc * cb[K * (p + g * LPS) + r + a * M];
+  CodebookLane<C> vsrc;
+  vsrc.init(cb, k.sc, p);
 
   // slot layout: lam history [L][BLOCK][KG] (8-byte entries), shift prefix N [L][SPB] (double)
   char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
@@ -260,14 +302,16 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       MT out[G][K];
       MT mx = (MT)-INFINITY;
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K];
+        vsrc.get(g, Vg);
 #pragma unroll
         for (int r = 0; r < K; ++r) {
           MT x[K];
           MT m = (MT)-INFINITY;
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            x[a] = emit<P>(u, V[g][r][a], lc[g][a], k.kap);
+            x[a] = emit<P>(u, Vg[r][a], lc[g][a], k.kap);
             m = tmax(m, x[a]);
           }
           float s = ex2((float)(x[0] - m));
@@ -276,6 +320,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           out[g][r] = m + (MT)lg2(s);
           mx = tmax(mx, out[g][r]);
         }
+      }
       if (t == L - 1) {
         MT v1[1] = {mx};
         chain_reduce<C, 1, 1u>(v1, red, rp);
@@ -331,23 +376,25 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       MT mx = (MT)-INFINITY;
       MT rout[G][K];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K];
+        vsrc.get(g, Vg);
 #pragma unroll
         for (int a = 0; a < K; ++a) {
           MT y[K];
           MT m = (MT)-INFINITY;
 #pragma unroll
           for (int r = 0; r < K; ++r) {
-            y[r] = emit<P>(u, V[g][r][a], rr[g][r], k.kap);
+            y[r] = emit<P>(u, Vg[r][a], rr[g][r], k.kap);
             m = tmax(m, y[r]);
           }
           float e0 = ex2((float)(y[0] - m));
-          float cs = e0, cw = V[g][0][a] * e0;
+          float cs = e0, cw = Vg[0][a] * e0;
 #pragma unroll
           for (int r = 1; r < K; ++r) {
             const float e = ex2((float)(y[r] - m));
             cs += e;
-            cw = __builtin_fmaf(V[g][r][a], e, cw);
+            cw = __builtin_fmaf(Vg[r][a], e, cw);
           }
           rout[g][a] = m + (MT)lg2(cs);
           mx = tmax(mx, rout[g][a]);
@@ -355,6 +402,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           num = __builtin_fmaf(f, cw, num);
           den = __builtin_fmaf(f, cs, den);
         }
+      }
       MT* mw = msg[mb] + q * M;
       if (t > 0) {
 #pragma unroll
@@ -423,16 +471,15 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
   const int p = LPS < 64 ? tid % LPS : tid;
   const float k2 = 2.0f * k.inv_t * k.csc;  // (2/T)(w - c) = k2 * (u - v)
 
-  float V[G][K][K], acc[G][K][K];
+  CodebookLane<C> vsrc;
+  vsrc.init(cb, k.sc, p);
+  float acc[G][K][K];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int r = 0; r < K; ++r)
 #pragma unroll
-      for (int a = 0; a < K; ++a) {
-        V[g][r][a] = k.sc * cb[K * (p + g * LPS) + r + a * M];
-        acc[g][r][a] = 0.f;
-      }
+      for (int a = 0; a < K; ++a) acc[g][r][a] = 0.f;
 
   // slot layout: lam history [L][BLOCK][KG] (8-byte entries), Phi history [L][BLOCK][KG]
   // (fp32), shift prefix N [L][SPB] (double)
@@ -477,28 +524,31 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int a = 0; a < K; ++a) pcc[g][a] = pc[g][a] - gwh;
       MT mx = (MT)-INFINITY;
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K];
+        vsrc.get(g, Vg);
 #pragma unroll
         for (int r = 0; r < K; ++r) {
           MT x[K];
           MT m = (MT)-INFINITY;
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            x[a] = emit<P>(u, V[g][r][a], lc[g][a], k.kap);
+            x[a] = emit<P>(u, Vg[r][a], lc[g][a], k.kap);
             m = tmax(m, x[a]);
           }
           float e0 = ex2((float)(x[0] - m));
-          float s = e0, ph = e0 * __builtin_fmaf(gtp, V[g][r][0], pcc[g][0]);
+          float s = e0, ph = e0 * __builtin_fmaf(gtp, Vg[r][0], pcc[g][0]);
 #pragma unroll
           for (int a = 1; a < K; ++a) {
             const float e = ex2((float)(x[a] - m));
             s += e;
-            ph = __builtin_fmaf(e, __builtin_fmaf(gtp, V[g][r][a], pcc[g][a]), ph);
+            ph = __builtin_fmaf(e, __builtin_fmaf(gtp, Vg[r][a], pcc[g][a]), ph);
           }
           out[g][r] = m + (MT)lg2(s);
           pout[g][r] = ph * rcp_nr(s);
           mx = tmax(mx, out[g][r]);
         }
+      }
       MT* mw = msgl[mb] + q * M;
       float* pw = msgp[mb] + q * M;
 #pragma unroll
@@ -562,7 +612,9 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       MT rout[G][K];
       float qout[G][K];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K];
+        vsrc.get(g, Vg);
 #pragma unroll
         for (int a = 0; a < K; ++a) {
           MT y[K];
@@ -570,15 +622,15 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           MT m = (MT)-INFINITY;
 #pragma unroll
           for (int r = 0; r < K; ++r) {
-            dd[r] = u - V[g][r][a];
-            y[r] = emit<P>(u, V[g][r][a], rr[g][r], k.kap);
+            dd[r] = u - Vg[r][a];
+            y[r] = emit<P>(u, Vg[r][a], rr[g][r], k.kap);
             m = tmax(m, y[r]);
           }
           float e[K], t2[K];
 #pragma unroll
           for (int r = 0; r < K; ++r) {
             e[r] = ex2((float)(y[r] - m));
-            t2[r] = __builtin_fmaf(gtp, V[g][r][a], qrc[g][r]);
+            t2[r] = __builtin_fmaf(gtp, Vg[r][a], qrc[g][r]);
           }
           float cs = e[0], ps = e[0] * t2[0];
 #pragma unroll
@@ -596,11 +648,12 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             for (int r = 0; r < K; ++r) {
               const float gm = e[r] * f;
               const float eh = gm * (t2[r] + pa);
-              gw = __builtin_fmaf(V[g][r][a], eh, gw);
+              gw = __builtin_fmaf(Vg[r][a], eh, gw);
               acc[g][r][a] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, acc[g][r][a]));
             }
           }
         }
+      }
       MT* mw = msgl[mb] + q * M;
       float* pw = msgp[mb] + q * M;
       if (t > 0) {

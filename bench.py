@@ -32,20 +32,55 @@ METRIC = "BCJR fwd+bwd trellis state-steps/sec (1 MI355X) + % of HBM/compute roo
 # the recursions, not from the compiled code; an FMA counts as one operation.
 #   forward  kernel: alpha side 4.5 VALU + 1.25 trans, beta side + posterior + w_hat 6.5 + 1.5
 #   backward kernel: alpha side + Phi 7.25 VALU + 1.5 trans, beta side + Psi + D + grads 15 + 1.75
-# Transcendentals (v_exp_f32, v_log_f32, v_rcp_f32) are quarter-rate: 4 lane-op slots each.
-# Peak: MI355X fp32 vector 157.3 TFLOP/s = 78.6 T lane-op slots/s (FMA = 2 flops).
+# Peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T VALU lane-op slots/s (one wave64
+# instruction per SIMD per 4 clocks; the 157.3 TFLOP/s fp32 figure is this rate x 4 flops of a
+# packed dual FMA, which this build does not use). Transcendentals (v_exp_f32, v_log_f32,
+# v_rcp_f32) issue at half rate on gfx950: 2 slots each (SQ_ACTIVE_INST_VALU against
+# SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 of the profiled kernels).
 # ---------------------------------------------------------------------------------------------
 OPS = {
     "fwd": {"valu": 4.5 + 6.5, "trans": 1.25 + 1.5},
     "bwd": {"valu": 7.25 + 15.0, "trans": 1.5 + 1.75},
 }
-TRANS_SLOTS = 4.0
-PEAK_TOPS = 157.3 / 2.0
+TRANS_SLOTS = 2.0
+PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+# HBM traffic of the profiled kernel, read from the committed rocprofv3 summary; reported only
+# while the kernel sources still hash to the value recorded there.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_sparse_bwd_llama32-1b-mlp-up-s4096_pmc.md")
+KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_decoding_amd/csrc/geom.h"]
 
 
 def op_slots(kernel: str) -> float:
     o = OPS[kernel]
     return o["valu"] + TRANS_SLOTS * o["trans"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload_name: str):
+    """HBM bytes per launch of the backward kernel from the committed counter summary, or None
+    if there is none for this workload or the kernel changed since it was taken."""
+    if not os.path.exists(TRAFFIC_PROFILE) or workload_name not in TRAFFIC_PROFILE:
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -56,7 +91,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--temp", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256, help="chains timed on the CPU oracle")
+    ap.add_argument("--cpu-sample", type=int, default=1536, help="chains timed on the CPU oracle")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -181,7 +216,7 @@ def main():
             "unit": "Tops/s",
             "frac": achieved / PEAK_TOPS,
             "ops_per_state_step": op_slots("bwd"),
-            "traffic": None,
+            "traffic": profiled_traffic(wl.name),
         },
     }
     if not args.no_cpu_baseline:
