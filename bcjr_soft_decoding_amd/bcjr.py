@@ -20,7 +20,9 @@ FWD, BWD, VIT = 0, 1, 2
 
 EXPORTED = (
     "bcjr_supported", "bcjr_saved_bytes", "bcjr_workspace_bytes", "bcjr_forward",
-    "bcjr_backward", "viterbi_decode", "bcjr_status_string",
+    "bcjr_backward", "viterbi_decode", "bcjr_dense_supported", "bcjr_dense_saved_bytes",
+    "bcjr_dense_workspace_bytes", "bcjr_dense_forward", "bcjr_dense_backward",
+    "bcjr_status_string",
 )
 
 
@@ -65,6 +67,16 @@ def lib() -> ctypes.CDLL:
     L.bcjr_backward.restype = ctypes.c_int
     L.viterbi_decode.argtypes = [TP, P, I64, I64, P, P, P, SZ, P]
     L.viterbi_decode.restype = ctypes.c_int
+    L.bcjr_dense_supported.argtypes = [I32]
+    L.bcjr_dense_supported.restype = ctypes.c_int
+    L.bcjr_dense_saved_bytes.argtypes = [I32, I64, I64]
+    L.bcjr_dense_saved_bytes.restype = SZ
+    L.bcjr_dense_workspace_bytes.argtypes = [I32, I64, I64, ctypes.c_int]
+    L.bcjr_dense_workspace_bytes.restype = SZ
+    L.bcjr_dense_forward.argtypes = [I32, P, P, P, I64, I64, F, P, P, P, P, SZ, P]
+    L.bcjr_dense_forward.restype = ctypes.c_int
+    L.bcjr_dense_backward.argtypes = [I32, P, P, P, I64, I64, F, P, P, P, P, P, P, P, SZ, P]
+    L.bcjr_dense_backward.restype = ctypes.c_int
     L.bcjr_status_string.argtypes = [ctypes.c_int]
     L.bcjr_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -172,3 +184,65 @@ def viterbi_decode(codebook, w, n, k, states=None, w_hard=None, want_w_hard=True
                               _ptr(ws), ws.numel(), _stream())
     _check(st, "viterbi_decode")
     return states, w_hard
+
+
+# ---- dense (fully connected) trellis ---------------------------------------------------------
+
+def bcjr_dense_supported(S: int) -> bool:
+    return bool(lib().bcjr_dense_supported(int(S)))
+
+
+def bcjr_dense_saved_bytes(S: int, B: int, L: int) -> int:
+    return int(lib().bcjr_dense_saved_bytes(int(S), B, L))
+
+
+def bcjr_dense_workspace_bytes(S: int, B: int, L: int, which: int) -> int:
+    return int(lib().bcjr_dense_workspace_bytes(int(S), B, L, which))
+
+
+def dense_workspace(S, B, L, which, device="cuda"):
+    """Allocate a device workspace of the queried size (uint8 tensor)."""
+    nb = bcjr_dense_workspace_bytes(S, B, L, which)
+    return torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+
+
+def bcjr_dense_forward(theta, codebook, w, T, w_hat=None, log_z=None, saved=None, ws=None):
+    """Dense trellis: soft codeword w_hat [B,L] and log Z [B]; returns (w_hat, log_z, saved)."""
+    _f32(theta, "theta"); _f32(codebook, "codebook"); _f32(w, "w")
+    S = codebook.numel()
+    B, L = w.shape
+    dev = w.device
+    w_hat = torch.empty_like(w) if w_hat is None else w_hat
+    log_z = torch.empty(B, dtype=torch.float32, device=dev) if log_z is None else log_z
+    if saved is None:
+        saved = torch.empty(max(bcjr_dense_saved_bytes(S, B, L), 1), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = dense_workspace(S, B, L, FWD, dev)
+    st = lib().bcjr_dense_forward(S, _ptr(theta), _ptr(codebook), _ptr(w), B, L, float(T),
+                                  _ptr(w_hat), _ptr(log_z), _ptr(saved), _ptr(ws), ws.numel(),
+                                  _stream())
+    _check(st, "bcjr_dense_forward")
+    return w_hat, log_z, saved
+
+
+def bcjr_dense_backward(theta, codebook, w, T, saved, grad_w_hat, grad_log_z=None, grad_w=None,
+                        grad_codebook=None, grad_theta=None, ws=None):
+    """Dense trellis gradient of sum(g * w_hat) + sum(h * log_z); returns
+    (grad_w, grad_codebook, grad_theta)."""
+    _f32(theta, "theta"); _f32(codebook, "codebook"); _f32(w, "w"); _f32(grad_w_hat, "grad_w_hat")
+    if grad_log_z is not None:
+        _f32(grad_log_z, "grad_log_z")
+    S = codebook.numel()
+    B, L = w.shape
+    dev = w.device
+    grad_w = torch.empty_like(w) if grad_w is None else grad_w
+    grad_codebook = torch.empty_like(codebook) if grad_codebook is None else grad_codebook
+    grad_theta = torch.empty_like(theta) if grad_theta is None else grad_theta
+    if ws is None:
+        ws = dense_workspace(S, B, L, BWD, dev)
+    st = lib().bcjr_dense_backward(S, _ptr(theta), _ptr(codebook), _ptr(w), B, L, float(T),
+                                   _ptr(saved), _ptr(grad_w_hat), _ptr(grad_log_z), _ptr(grad_w),
+                                   _ptr(grad_codebook), _ptr(grad_theta), _ptr(ws), ws.numel(),
+                                   _stream())
+    _check(st, "bcjr_dense_backward")
+    return grad_w, grad_codebook, grad_theta

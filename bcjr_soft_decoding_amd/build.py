@@ -28,7 +28,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-Wno-unknown-pragmas",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip"]
+SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kernels.hip"]
 
 
 def _compile(src: str) -> str:

@@ -80,6 +80,15 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
 
 bcjr_status from_hip(int e) { return e == 0 ? BCJR_OK : BCJR_E_DEVICE; }
 
+// Dense shapes: S >= 1, B >= 0, L >= 1, and every [B, L, S] array addressable with 64-bit
+// offsets (B * L * S * 16 bytes below 2^62).
+bcjr_status dense_check(int32_t S, int64_t B, int64_t L) {
+  if (S < 1 || S > 65536 || B < 0 || L < 1) return BCJR_E_SHAPE;
+  if (B > 0 && (L > ((int64_t)1 << 40) / B || B * L > ((int64_t)1 << 58) / S)) return BCJR_E_SHAPE;
+  if (!dense_shape_built(S)) return BCJR_E_UNSUPPORTED;
+  return BCJR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,6 +165,62 @@ bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, in
   const size_t need = sparse_vit_ws_bytes(g, L);
   if (!ws_ok(ws, ws_bytes, need)) return BCJR_E_WORKSPACE;
   return from_hip(launch_viterbi(g, tr->codebook, w, B, L, states, w_hard, ws, stream));
+}
+
+int bcjr_dense_supported(int32_t S) { return S >= 1 && S <= 65536 && dense_shape_built(S) ? 1 : 0; }
+
+size_t bcjr_dense_saved_bytes(int32_t S, int64_t B, int64_t L) {
+  if (dense_check(S, B, L) != BCJR_OK) return 0;
+  DenseLayout d;
+  dense_layout(S, B, L, &d);
+  return d.saved;
+}
+
+size_t bcjr_dense_workspace_bytes(int32_t S, int64_t B, int64_t L, int which) {
+  if (dense_check(S, B, L) != BCJR_OK || which < 0 || which > 1 || B == 0) return 0;
+  DenseLayout d;
+  dense_layout(S, B, L, &d);
+  return which == 0 ? d.fwd : d.bwd;
+}
+
+bcjr_status bcjr_dense_forward(int32_t S, const float* theta, const float* codebook, const float* w,
+                               int64_t B, int64_t L, float T, float* w_hat, float* log_z,
+                               void* saved, void* ws, size_t ws_bytes, bcjr_stream_t stream) {
+  bcjr_status st = dense_check(S, B, L);
+  if (st != BCJR_OK) return st;
+  if (!temp_ok(T)) return BCJR_E_ARG;
+  if (B == 0) return BCJR_OK;
+  if (!theta || !codebook || !w || !w_hat || !log_z || !saved) return BCJR_E_ARG;
+  if (((uintptr_t)saved & 15) != 0) return BCJR_E_ARG;
+  DenseLayout d;
+  dense_layout(S, B, L, &d);
+  if (!ws_ok(ws, ws_bytes, d.fwd)) return BCJR_E_WORKSPACE;
+  return from_hip(launch_dense_forward(S, theta, codebook, w, B, L, T, w_hat, log_z, saved, ws,
+                                       stream));
+}
+
+bcjr_status bcjr_dense_backward(int32_t S, const float* theta, const float* codebook,
+                                const float* w, int64_t B, int64_t L, float T, const void* saved,
+                                const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                                float* grad_codebook, float* grad_theta, void* ws, size_t ws_bytes,
+                                bcjr_stream_t stream) {
+  bcjr_status st = dense_check(S, B, L);
+  if (st != BCJR_OK) return st;
+  if (!temp_ok(T)) return BCJR_E_ARG;
+  if (!grad_codebook || !grad_theta) return BCJR_E_ARG;
+  if (B == 0) {
+    // no chain contributes: both summed gradients are zero
+    int e = launch_fill_zero(grad_codebook, S, stream);
+    if (e == 0) e = launch_fill_zero(grad_theta, (int64_t)S * S, stream);
+    return from_hip(e);
+  }
+  if (!theta || !codebook || !w || !saved || !grad_w_hat || !grad_w) return BCJR_E_ARG;
+  if (((uintptr_t)saved & 15) != 0) return BCJR_E_ARG;
+  DenseLayout d;
+  dense_layout(S, B, L, &d);
+  if (!ws_ok(ws, ws_bytes, d.bwd)) return BCJR_E_WORKSPACE;
+  return from_hip(launch_dense_backward(S, theta, codebook, w, B, L, T, saved, grad_w_hat,
+                                        grad_log_z, grad_w, grad_codebook, grad_theta, ws, stream));
 }
 
 const char* bcjr_status_string(bcjr_status s) {

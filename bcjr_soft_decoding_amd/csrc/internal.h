@@ -70,4 +70,52 @@ int resident_grid(const void* kernel, int block, int64_t slots);
 int launch_viterbi(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                    int64_t L, int32_t* states, float* w_hard, void* ws, void* stream);
 
+// ---- dense (fully connected) trellis -------------------------------------------------------
+// Sweep kernels use one persistent block per 4 chains, at most kDenseSweepMaxGrid blocks; the
+// theta-gradient product at most kDenseGemmMaxGrid blocks. Both bounds size workspace partials.
+constexpr int64_t kDenseSweepMaxGrid = 1024;
+constexpr int64_t kDenseGemmMaxGrid = 512;
+inline int64_t dense_sweep_slots(int64_t units) {
+  return units < kDenseSweepMaxGrid ? units : kDenseSweepMaxGrid;
+}
+
+// Byte offsets of the dense context (`saved`) and workspace. saved: log2 Z [B] (double), the
+// per-step scalars [B, L, 4] (w_hat_t, 1/zz_t, ref_t, 1/n_{t-1}), the forward messages a and the
+// backward messages u, each [B, L, S]. Workspace: the transition matrix M [S, S] and kappa * cm
+// [S] (forward and backward); the backward adds L1, R1, R2 [B, L, S], the codebook-gradient
+// partials of its two sweeps [2, kDenseSweepMaxGrid, S] and the theta-gradient partials
+// [kDenseGemmMaxGrid, S, S].
+struct DenseLayout {
+  size_t lz2, pack, ha, hb, saved;
+  size_t mat, cmk, fwd, l1, r1, r2, gcp, gp, bwd;
+};
+inline void dense_layout(int S, int64_t B, int64_t L, DenseLayout* d) {
+  const size_t bl = (size_t)B * (size_t)L;
+  const size_t bls = bl * (size_t)S * sizeof(float);
+  d->lz2 = 0;
+  d->pack = round256((size_t)B * sizeof(double));
+  d->ha = d->pack + round256(bl * 4 * sizeof(float));
+  d->hb = d->ha + round256(bls);
+  d->saved = d->hb + round256(bls);
+  d->mat = 0;
+  d->cmk = round256((size_t)S * S * sizeof(float));
+  d->fwd = d->cmk + round256((size_t)S * sizeof(float));
+  d->l1 = d->fwd;
+  d->r1 = d->l1 + round256(bls);
+  d->r2 = d->r1 + round256(bls);
+  d->gcp = d->r2 + round256(bls);
+  d->gp = d->gcp + round256((size_t)2 * kDenseSweepMaxGrid * S * sizeof(float));
+  d->bwd = d->gp + round256((size_t)kDenseGemmMaxGrid * S * S * sizeof(float));
+}
+
+// True if dense kernels for S states are compiled in (dense_kernels.hip).
+bool dense_shape_built(int S);
+int launch_dense_forward(int S, const float* theta, const float* codebook, const float* w, int64_t B,
+                         int64_t L, float T, float* w_hat, float* log_z, void* saved, void* ws,
+                         void* stream);
+int launch_dense_backward(int S, const float* theta, const float* codebook, const float* w,
+                          int64_t B, int64_t L, float T, const void* saved, const float* grad_w_hat,
+                          const float* grad_log_z, float* grad_w, float* grad_codebook,
+                          float* grad_theta, void* ws, void* stream);
+
 }  // namespace bcjr

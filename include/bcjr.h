@@ -66,11 +66,10 @@ typedef struct {
 /* Query: 1 if a kernel exists for this (n, k, V), else 0. Host only. */
 int bcjr_supported(const bcjr_trellis* tr);
 
-/* Bytes of the forward -> backward context: the forward's per-chain log2 Z (as an exact
- * integer part and a fraction, fp32 [B][2]), which
- * the backward uses to normalise the posteriors, and its soft codeword (fp32 [B,L]), on which
- * the backward centres its conditional expectations. Returns 0 for an invalid shape. Host
- * only, needs no device. */
+/* Bytes of the forward -> backward context: the forward's per-chain log2 Z (double [B], padded
+ * to a multiple of 32), which the backward uses to normalise the posteriors, and its soft
+ * codeword (fp32 [B,L]), on which the backward centres its conditional expectations. Returns 0
+ * for an invalid shape. Host only, needs no device. */
 size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L);
 
 /* Bytes of device workspace for a call: which = 0 forward, 1 backward, 2 viterbi.
@@ -125,6 +124,65 @@ bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int
 bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
                            int32_t* states, float* w_hard, void* ws, size_t ws_bytes,
                            bcjr_stream_t stream);
+
+/* ---- Dense (fully connected) trellis --------------------------------------------------------
+ * Every state may follow every state; theta [S,S] (DEVICE, row-major, theta[s*S + s'] for the
+ * transition s -> s') holds transition log-potentials. A path's weight is
+ *   exp( ( sum_{t>=1} theta(s_{t-1}, s_t) - sum_t (w_t - c(s_t))^2 ) / T ),
+ * free start and free end state. This is the transfer-matrix form of the method (abstract: the
+ * computation is identical to the transfer matrix of a 1D Ising-like chain; technical summary,
+ * "Key technical innovations": O(L*S^2) forward-backward with exact gradients through the
+ * trellis parameters), run as rescaled linear-domain matrix products on the matrix cores.
+ * Messages are fp32 in the linear domain, rescaled every step; a state whose relative weight
+ * falls below the fp32 range (2^-126 of the step's best) is dropped. Intended for moderate T
+ * (validated for T in [0.1, 5] with theta, c and w of unit scale); use the bitshift entry points
+ * for the near-hard regime.
+ * Supported S: 32, 64, 128, 256 (bcjr_dense_supported). B >= 0, L >= 1.
+ */
+
+/* 1 if dense kernels exist for S states, else 0. Host only. */
+int bcjr_dense_supported(int32_t S);
+
+/* Bytes of the dense forward -> backward context: log2 Z per chain (double [B]), per-step
+ * scalars (fp32 [B,L,4]) and the forward and backward message histories (fp32 [B,L,S] each).
+ * 0 for an invalid or unsupported shape. Host only. The context must be 16-byte aligned. */
+size_t bcjr_dense_saved_bytes(int32_t S, int64_t B, int64_t L);
+
+/* Bytes of dense workspace: which = 0 forward (the transition matrix), 1 backward (adds three
+ * [B,L,S] fp32 operand arrays of the theta gradient and fixed-size partial sums). 0 for an
+ * invalid shape, an unsupported S, a bad flag or B = 0. Host only. */
+size_t bcjr_dense_workspace_bytes(int32_t S, int64_t B, int64_t L, int which);
+
+/*
+ * Dense forward: soft codeword and log partition function, as bcjr_forward.
+ * theta    DEVICE [S,S] read only;  codebook DEVICE [S];  w DEVICE [B,L]
+ * w_hat    DEVICE [B,L] written;    log_z DEVICE [B] written
+ * saved    DEVICE, bcjr_dense_saved_bytes() bytes, 16-byte aligned, written
+ * ws       DEVICE, ws_bytes >= bcjr_dense_workspace_bytes(S, B, L, 0)
+ * Errors: BCJR_E_SHAPE (S < 1, B < 0, L < 1, sizes beyond 64-bit offsets), BCJR_E_UNSUPPORTED
+ * (no kernel for S), BCJR_E_ARG (null pointer with B > 0, misaligned saved, bad T),
+ * BCJR_E_WORKSPACE. B = 0 enqueues nothing.
+ */
+bcjr_status bcjr_dense_forward(int32_t S, const float* theta, const float* codebook, const float* w,
+                               int64_t B, int64_t L, float T, float* w_hat, float* log_z,
+                               void* saved, void* ws, size_t ws_bytes, bcjr_stream_t stream);
+
+/*
+ * Dense backward: gradient of F = sum g w_hat + sum h log_z (as bcjr_backward) with respect to
+ * w, the codebook and theta.
+ * saved       DEVICE, written by bcjr_dense_forward with the same S, theta, codebook, w, B, L, T
+ * grad_w_hat  DEVICE [B,L];  grad_log_z DEVICE [B] or NULL (h = 0)
+ * grad_w      DEVICE [B,L] written
+ * grad_codebook DEVICE [S] written, grad_theta DEVICE [S,S] written (both overwritten and summed
+ *             over all B chains in a fixed order)
+ * ws          DEVICE, ws_bytes >= bcjr_dense_workspace_bytes(S, B, L, 1)
+ * B = 0 writes zeros to grad_codebook and grad_theta.
+ */
+bcjr_status bcjr_dense_backward(int32_t S, const float* theta, const float* codebook,
+                                const float* w, int64_t B, int64_t L, float T, const void* saved,
+                                const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                                float* grad_codebook, float* grad_theta, void* ws, size_t ws_bytes,
+                                bcjr_stream_t stream);
 
 /* Text of a status code (static storage). */
 const char* bcjr_status_string(bcjr_status s);

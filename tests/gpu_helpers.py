@@ -25,8 +25,10 @@ def assert_normwise(x, ref, rtol, what=""):
     ref = np.asarray(ref, np.float64)
     assert x.shape == ref.shape, (what, x.shape, ref.shape)
     assert np.all(np.isfinite(x)), f"{what}: non-finite values"
-    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref * ref)))
-    err = np.abs(x - ref) / scale
+    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref * ref))) if ref.size else ref
+    diff = np.abs(x - ref)
+    # an all-zero reference must be matched exactly
+    err = np.where(scale > 0, diff / np.where(scale > 0, scale, 1.0), np.where(diff == 0, 0.0, np.inf))
     worst = float(err.max()) if err.size else 0.0
     assert worst <= rtol, f"{what}: worst normwise error {worst:.3e} > {rtol:.1e}"
     return worst

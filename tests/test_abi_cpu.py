@@ -122,3 +122,62 @@ def test_backward_and_viterbi_reject_bad_arguments_without_device(lib):
     assert vit(wsb=1) == bcjr.BCJR_E_WORKSPACE
     assert vit(B=-2) == bcjr.BCJR_E_SHAPE
     assert vit(B=0, st=P(0), ws=P(0), wsb=0) == bcjr.BCJR_OK
+
+
+def test_dense_size_queries(lib):
+    for S in (32, 64, 128, 256):
+        assert bcjr.bcjr_dense_supported(S)
+    for S in (0, 16, 48, 512):
+        assert not bcjr.bcjr_dense_supported(S)
+    S, B, L = 256, 1024, 1024
+    sv = bcjr.bcjr_dense_saved_bytes(S, B, L)
+    # two [B, L, S] fp32 message histories dominate the context
+    assert 2 * B * L * S * 4 + 16 * B * L <= sv < 2 * B * L * S * 4 + 16 * B * L + 4096 + 8 * B
+    f = bcjr.bcjr_dense_workspace_bytes(S, B, L, 0)
+    b = bcjr.bcjr_dense_workspace_bytes(S, B, L, 1)
+    assert 0 < f < b and b >= 3 * B * L * S * 4
+    assert bcjr.bcjr_dense_workspace_bytes(S, B, L, 2) == 0
+    assert bcjr.bcjr_dense_workspace_bytes(48, B, L, 0) == 0
+    assert bcjr.bcjr_dense_workspace_bytes(S, 0, L, 1) == 0
+    assert bcjr.bcjr_dense_saved_bytes(S, -1, L) == 0
+    assert bcjr.bcjr_dense_saved_bytes(S, B, 0) == 0
+
+
+def test_dense_rejects_bad_arguments_without_device(lib):
+    P = ctypes.c_void_p
+    ok = dict(th=P(0x1000), cb=P(0x1100), w=P(0x2000), wh=P(0x3000), lz=P(0x4000), sv=P(0x5000),
+              ws=P(0x6000), g=P(0x7000), gw=P(0x8000), gc=P(0x9000), gt=P(0xA000))
+
+    def fwd(S=64, B=4, L=8, T=0.5, wsb=1 << 40, **kw):
+        a = dict(ok, **kw)
+        return lib.bcjr_dense_forward(S, a["th"], a["cb"], a["w"], B, L, T, a["wh"], a["lz"],
+                                      a["sv"], a["ws"], wsb, None)
+
+    def bwd(S=64, B=4, L=8, T=0.5, wsb=1 << 40, **kw):
+        a = dict(ok, **kw)
+        return lib.bcjr_dense_backward(S, a["th"], a["cb"], a["w"], B, L, T, a["sv"], a["g"], None,
+                                       a["gw"], a["gc"], a["gt"], a["ws"], wsb, None)
+
+    assert fwd(S=0) == bcjr.BCJR_E_SHAPE
+    assert fwd(B=-1) == bcjr.BCJR_E_SHAPE
+    assert fwd(L=0) == bcjr.BCJR_E_SHAPE
+    assert fwd(B=1 << 40, L=1 << 30) == bcjr.BCJR_E_SHAPE
+    assert fwd(S=48) == bcjr.BCJR_E_UNSUPPORTED
+    assert fwd(T=0.0) == bcjr.BCJR_E_ARG
+    assert fwd(T=float("nan")) == bcjr.BCJR_E_ARG
+    assert fwd(th=P(0)) == bcjr.BCJR_E_ARG
+    assert fwd(cb=P(0)) == bcjr.BCJR_E_ARG
+    assert fwd(sv=P(0x5004)) == bcjr.BCJR_E_ARG  # context must be 16-byte aligned
+    assert fwd(ws=P(0)) == bcjr.BCJR_E_WORKSPACE
+    assert fwd(ws=P(0x6008)) == bcjr.BCJR_E_WORKSPACE
+    need = bcjr.bcjr_dense_workspace_bytes(64, 4, 8, 0)
+    assert fwd(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
+    assert fwd(B=0, th=P(0), w=P(0), wh=P(0), lz=P(0), sv=P(0), ws=P(0), wsb=0) == bcjr.BCJR_OK
+
+    assert bwd(T=-1.0) == bcjr.BCJR_E_ARG
+    assert bwd(gt=P(0)) == bcjr.BCJR_E_ARG
+    assert bwd(gc=P(0)) == bcjr.BCJR_E_ARG
+    assert bwd(g=P(0)) == bcjr.BCJR_E_ARG
+    assert bwd(S=100) == bcjr.BCJR_E_UNSUPPORTED
+    need = bcjr.bcjr_dense_workspace_bytes(64, 4, 8, 1)
+    assert bwd(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
