@@ -33,17 +33,18 @@
 //
 // Kernels: k_dense_prep (M, kappa cm), four sweeps (alpha and beta in the forward call; Psi then
 // Phi in the backward call), k_dense_theta_gemm (the theta gradient as one split-K product over
-// all chains and steps) and k_dense_finalize (fixed-order sums of the block partials).
+// all chains and steps) and k_dense_sum_parts (fixed-order sums of the block partials).
 //
 // Sweep tiling: one block per 4 chains, S/32 waves; wave wv owns output states 32wv..32wv+31.
 // The step product runs on v_mfma_f32_4x4x1f32 (16 independent 4x4 outer products): block b of
 // an instruction takes chain i = lane & 3, input state k = 4 kc + (lane >> 4) and output state
 // 32 wv + 16 set + (lane & 15), so lane l keeps M[4kc + l/16][32wv + 16set + l%16] (the
 // transposed entry for the backward sweeps) in registers for the whole launch: the matrix lives
-// in the register files of one block. The four partial sums over k (lane bits 4 and 5) are
-// folded with v_permlane32_swap / v_permlane16_swap as a reduce-scatter, which leaves each lane
-// with two (chain, state) results. Messages are staged in LDS as [k % 4][chain][k / 4] so that a
-// lane reads four consecutive MFMA operands with one 16-byte load.
+// in the register files of one block. The four partial sums over k (lane bits 4 and 5) of each
+// 16-state set are folded with v_permlane32_swap / v_permlane16_swap as a reduce-scatter, which
+// leaves lane l with chain l >> 4 at two states, so per-chain sums over states are 16-lane row
+// reductions. Messages are staged in LDS as [k % 4][chain][k / 4] so that a lane reads four
+// consecutive MFMA operands with one 16-byte load.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -117,11 +118,20 @@ struct DGeo {
   static_assert(S >= 32 && S <= 256 && (S & (S - 1)) == 0, "S must be 32, 64, 128 or 256");
 };
 
-// out[chain 2*bit4 + r][state 32wv + 16*bit5 + (lane & 15)] of the product of the staged message
-// (4 chains) with the register-resident matrix.
+// Reduce the four k-partials of one 16-state set (lane bits 4 and 5) and scatter the chains:
+// returns out[chain lane >> 4][state (lane & 15) of the set].
+__device__ __forceinline__ float scatter_set(const f4 s) {
+  const P2 a = swap32(s[0], s[2]);  // lanes 0-31 keep chain 0, lanes 32-63 chain 2
+  const P2 b = swap32(s[1], s[3]);  // chain 1, chain 3
+  const P2 q = swap16(a.lo + a.hi, b.lo + b.hi);
+  return q.lo + q.hi;
+}
+
+// Product of the staged message (4 chains) with the register-resident matrix. Lane l gets chain
+// l >> 4 at states 32wv + (l & 15) (o[0]) and 32wv + 16 + (l & 15) (o[1]).
 template <class C>
 __device__ __forceinline__ void product(const float* __restrict__ xs, const float (&m)[C::MR], int l,
-                                        float& o0, float& o1) {
+                                        float (&o)[2]) {
   const float* xr = xs + ((l >> 4) * 4 + (l & 3)) * C::XSTR;
   f4 acc[2][2];
 #pragma unroll
@@ -135,51 +145,32 @@ __device__ __forceinline__ void product(const float* __restrict__ xs, const floa
       acc[1][e & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], m[2 * (kc + e) + 1], acc[1][e & 1], 0, 0, 0);
     }
   }
-  const f4 s0 = acc[0][0] + acc[0][1];
-  const f4 s1 = acc[1][0] + acc[1][1];
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const P2 r = swap32(s0[i], s1[i]);  // lanes 0-31 keep set 0, lanes 32-63 set 1
-    v[i] = r.lo + r.hi;
-  }
-  const P2 r0 = swap16(v[0], v[2]);  // rows 0, 2 keep chain 0; rows 1, 3 chain 2
-  const P2 r1 = swap16(v[1], v[3]);
-  o0 = r0.lo + r0.hi;
-  o1 = r1.lo + r1.hi;
+  o[0] = scatter_set(acc[0][0] + acc[0][1]);
+  o[1] = scatter_set(acc[1][0] + acc[1][1]);
 }
 
-// Block-wide reduction of per-chain quantities over the S states. v[q][r] is this lane's value
-// of quantity q for chain ch0 + r; bit q of MAXQ selects a max instead of a sum. Returns the
-// block totals for the lane's two chains in out[q][r]. Contains the step's barrier.
+// Block-wide reduction of per-chain quantities over the S states, in two halves around the
+// step's barrier. publish(): v[q] is this lane's value of quantity q for its chain (lane >> 4,
+// already combined over the lane's two states); bit q of MAXQ selects a max instead of a sum;
+// the wave totals go to red[(q * 4 + chain) * NW + wave]. collect(), after the barrier: the
+// block total for the lane's chain in out[q].
 template <int NQR, int MAXQ, int NW>
-__device__ __forceinline__ void chain_reduce(const float (&v)[NQR][2], float* __restrict__ red, int l,
-                                             int wv, float (&out)[NQR][2]) {
+__device__ __forceinline__ void publish(const float (&v)[NQR], float* __restrict__ red, int l, int wv) {
 #pragma unroll
   for (int q = 0; q < NQR; ++q) {
-    float tot;
-    if ((MAXQ >> q) & 1) {
-      const P2 r = swap32(row_red<true>(v[q][0]), row_red<true>(v[q][1]));
-      tot = fmaxf(r.lo, r.hi);
-    } else {
-      const P2 r = swap32(row_red<false>(v[q][0]), row_red<false>(v[q][1]));
-      tot = r.lo + r.hi;
-    }
-    // lanes 0, 16, 32, 48 hold chains 0, 2, 1, 3
-    if ((l & 15) == 0) red[(q * 4 + 2 * ((l >> 4) & 1) + (l >> 5)) * NW + wv] = tot;
+    const float tot = ((MAXQ >> q) & 1) ? row_red<true>(v[q]) : row_red<false>(v[q]);
+    if ((l & 15) == 0) red[(q * 4 + (l >> 4)) * NW + wv] = tot;
   }
-  __syncthreads();
+}
+template <int NQR, int MAXQ, int NW>
+__device__ __forceinline__ void collect(const float* __restrict__ red, int l, float (&out)[NQR]) {
   const float x = l < NQR * 4 * NW ? red[l] : 0.f;
   const float sx = group_red<NW, false>(x);
   const float mx = group_red<NW, true>(x);
   const int ql = l / (4 * NW);
   const float tot = ((MAXQ >> ql) & 1) ? mx : sx;
-  const int ch0 = 2 * ((l >> 4) & 1);
 #pragma unroll
-  for (int q = 0; q < NQR; ++q) {
-    out[q][0] = __shfl(tot, (q * 4 + ch0) * NW, 64);
-    out[q][1] = __shfl(tot, (q * 4 + ch0 + 1) * NW, 64);
-  }
+  for (int q = 0; q < NQR; ++q) out[q] = __shfl(tot, (q * 4 + (l >> 4)) * NW, 64);
 }
 
 struct SweepArgs {
@@ -236,10 +227,14 @@ k_dense_sweep(SweepArgs A) {
   __shared__ __attribute__((aligned(16))) float sc[2][NSC];
 
   const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
-  const int col = 32 * wv + (l & 15) + 16 * (l >> 5);
-  const int ch0 = 2 * ((l >> 4) & 1);
-  const float cc = A.cb[col];
-  const float cmk = A.cmk[col];
+  const int ch = l >> 4;                  // chain of this lane within a unit of 4
+  const int col0 = 32 * wv + (l & 15);    // this lane's states: col0 and col0 + 16
+  float cc[2], ck[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    cc[e] = A.cb[col0 + 16 * e];
+    ck[e] = A.cmk[col0 + 16 * e];
+  }
   const float kap = A.kap;
   const long long L = A.L, B = A.B;
   const long long nch = (L + kChunk - 1) / kChunk;
@@ -253,21 +248,16 @@ k_dense_sweep(SweepArgs A) {
       const int o = 32 * wv + 16 * set + (l & 15);
       m[2 * kc + set] = FWD ? A.mat[k * S + o] : A.mat[o * S + k];
     }
-  // where this lane stages its two values (state col, chains ch0 and ch0 + 1)
-  const int xo = ((col & 3) * 4 + ch0) * C::XSTR + (col >> 2);
-  float gc = 0.f;
+  // where this lane stages its values: X[ch][k] at ((k % 4) * 4 + ch) * XSTR + k / 4
+  const int xo = ((col0 & 3) * 4 + ch) * C::XSTR + (col0 >> 2);  // state col0 + 16: xo + 4
+  float gc[2] = {0.f, 0.f};
 
   for (long long unit = blockIdx.x; unit < A.units; unit += gridDim.x) {
     const long long b0 = unit * 4;
-    const long long bA = b0 + ch0 < B ? b0 + ch0 : B - 1;
-    const long long bB = b0 + ch0 + 1 < B ? b0 + ch0 + 1 : B - 1;
-    const bool vA = b0 + ch0 < B, vB = b0 + ch0 + 1 < B;
-    const float fA = vA ? 1.f : 0.f, fB = vB ? 1.f : 0.f;
-    float hA = 0.f, hB = 0.f;
-    if ((MODE == kPsi || MODE == kPhi) && A.h != nullptr) {
-      hA = A.h[bA];
-      hB = A.h[bB];
-    }
+    const bool valid = b0 + ch < B;
+    const long long b = valid ? b0 + ch : B - 1;
+    const float fv = valid ? 1.f : 0.f;
+    const float hh = ((MODE == kPsi || MODE == kPhi) && A.h != nullptr) ? A.h[b] : 0.f;
 
     float sr[NPT];
     auto stage_load = [&](long long c) {
@@ -276,10 +266,10 @@ k_dense_sweep(SweepArgs A) {
         const int idx = tid + p * C::BLOCK;
         sr[p] = 0.f;
         if (idx < NSC) {
-          const int tt = idx / (NQ * 4), q = (idx >> 2) % NQ, ch = idx & 3;
+          const int tt = idx / (NQ * 4), q = (idx >> 2) % NQ, cq = idx & 3;
           const long long j = c * kChunk + tt;
-          const long long b = b0 + ch < B ? b0 + ch : B - 1;
-          if (j < L) sr[p] = fetch_scalar<MODE>(A, q, b, FWD ? j : L - 1 - j);
+          const long long bq = b0 + cq < B ? b0 + cq : B - 1;
+          if (j < L) sr[p] = fetch_scalar<MODE>(A, q, bq, FWD ? j : L - 1 - j);
         }
       }
     };
@@ -293,12 +283,12 @@ k_dense_sweep(SweepArgs A) {
     auto hist_load = [&](long long j, float (&ra)[2], float (&rb)[2]) {
       if (MODE == kAlpha || j >= L) return;
       const long long t = FWD ? j : L - 1 - j;
-      const long long iA = (bA * L + t) * S + col, iB = (bB * L + t) * S + col;
-      ra[0] = A.ha[iA];
-      ra[1] = A.ha[iB];
+      const long long i0 = (b * L + t) * S + col0;
+      ra[0] = A.ha[i0];
+      ra[1] = A.ha[i0 + 16];
       if (MODE == kPsi || MODE == kPhi) {
-        rb[0] = A.hb[iA];
-        rb[1] = A.hb[iB];
+        rb[0] = A.hb[i0];
+        rb[1] = A.hb[i0 + 16];
       }
     };
 
@@ -308,180 +298,160 @@ k_dense_sweep(SweepArgs A) {
     __syncthreads();
 
     // per-chain state carried between steps
-    float ellA = 0.f, ellB = 0.f, refA = 0.f, refB = 0.f;  // alpha: emission and shift of step t
-    float sA = 1.f, sB = 1.f;                              // scale of the next product output
-    double lzA = 0.0, lzB = 0.0;                           // alpha: log2 Z
+    float ell[2] = {0.f, 0.f}, ref = 0.f;  // alpha: emission and shift of step t
+    float nl[2] = {0.f, 0.f};              // alpha: emission of the step after
+    float sc_prev = 1.f;                   // scale of the next product output
+    float p_wh = 0.f, p_wt = 0.f;          // Psi: w_hat_t and w_t of the step awaiting its sum
+    double lz = 0.0;                       // alpha: log2 Z
     if (MODE == kAlpha) {
-      const float d0 = A.w[bA * L] - cc, d1 = A.w[bB * L] - cc;
-      ellA = -kap * d0 * d0;
-      ellB = -kap * d1 * d1;
-      const float v[1][2] = {{ellA, ellB}};
-      float out[1][2];
-      chain_reduce<1, 1, C::NW>(v, red[1], l, wv, out);
-      refA = out[0][0];
-      refB = out[0][1];
+      const float w0 = A.w[b * L];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float d = w0 - cc[e];
+        ell[e] = -kap * d * d;
+      }
+      const float v[1] = {fmaxf(ell[0], ell[1])};
+      float out[1];
+      publish<1, 1, C::NW>(v, red[1], l, wv);
+      __syncthreads();
+      collect<1, 1, C::NW>(red[1], l, out);
+      ref = out[0];
     }
+
+    // Per-chain sums of step jp, published before the barrier that ended it, are collected in
+    // the next step after its product has been issued, so that they overlap the matrix work.
+    auto finish = [&](long long jp) {
+      const long long tp = FWD ? jp : L - 1 - jp;
+      const long long itp = b * L + tp;
+      const bool writer = wv == 0 && (l & 15) == 0 && valid;  // one lane per chain
+      if constexpr (MODE == kAlpha) {
+        float out[2];
+        collect<2, 2, C::NW>(red[jp & 1], l, out);
+        sc_prev = 1.f / out[0];
+        lz += (double)ref + (double)lg2(out[0]);
+        if (writer) {
+          A.pack[itp * 4 + 2] = ref;
+          if (tp == 0) A.pack[itp * 4 + 3] = 1.f;
+          if (tp + 1 < L) A.pack[(itp + 1) * 4 + 3] = sc_prev;
+        }
+        ref = out[1];
+        ell[0] = nl[0];
+        ell[1] = nl[1];
+      } else if constexpr (MODE == kBeta) {
+        float out[2];
+        collect<2, 0, C::NW>(red[jp & 1], l, out);
+        sc_prev = 1.f / out[0];
+        if (writer) {
+          const float wh = out[1] / out[0];
+          A.pack[itp * 4 + 0] = wh;
+          A.pack[itp * 4 + 1] = sc_prev;
+          A.w_hat[itp] = wh;
+        }
+      } else if constexpr (MODE == kPsi) {
+        float out[1];
+        collect<1, 0, C::NW>(red[jp & 1], l, out);
+        if (writer) A.grad_w[itp] = A.two_t * (out[0] + hh * (p_wh - p_wt));
+      } else {
+        float out[1];
+        collect<1, 0, C::NW>(red[jp & 1], l, out);
+        if (writer) A.grad_w[itp] += A.two_t * out[0];
+      }
+    };
 
     auto step = [&](long long j, float (&ra)[2], float (&rb)[2]) {
       const long long t = FWD ? j : L - 1 - j;
       const int buf = (int)(j & 1);
       const long long cidx = j / kChunk;
       const int tt = (int)(j - cidx * kChunk);
-      const float* scb = sc[cidx & 1] + tt * NQ * 4 + ch0;
-      float o0 = 0.f, o1 = 0.f;
-      if (j > 0) product<C>(xs[buf ^ 1], m, l, o0, o1);
+      const float* scb = sc[cidx & 1] + tt * NQ * 4 + ch;
+      float o[2] = {0.f, 0.f};
+      if (j > 0) {
+        product<C>(xs[buf ^ 1], m, l, o);
+        finish(j - 1);
+      }
       float* xw = xs[buf] + xo;
-      const long long iA = bA * L + t, iB = bB * L + t;
-      const bool last = tt == kChunk - 1 && cidx + 1 < nch;
+      const long long i0 = (b * L + t) * S + col0;
 
       if constexpr (MODE == kAlpha) {
-        const float aA = (j > 0 ? o0 * sA : 1.f) * ex2(ellA - refA);
-        const float aB = (j > 0 ? o1 * sB : 1.f) * ex2(ellB - refB);
-        xw[0] = aA;
-        xw[C::XSTR] = aB;
-        if (vA) A.ha[iA * S + col] = aA;
-        if (vB) A.ha[iB * S + col] = aB;
-        const f2 wn = *reinterpret_cast<const f2*>(scb);  // w_{t+1}
-        const float dA = wn[0] - cc, dB = wn[1] - cc;
-        const float nA = cmk - kap * dA * dA, nB = cmk - kap * dB * dB;
-        const float v[2][2] = {{aA, aB}, {nA, nB}};
-        float out[2][2];
-        if (last) stage_store((int)((cidx + 1) & 1));
-        chain_reduce<2, 2, C::NW>(v, red[buf], l, wv, out);
-        if (tt == 0 && cidx + 1 < nch) stage_load(cidx + 1);
-        sA = 1.f / out[0][0];
-        sB = 1.f / out[0][1];
-        lzA += (double)refA + (double)lg2(out[0][0]);
-        lzB += (double)refB + (double)lg2(out[0][1]);
-        if (wv == 0 && (l & 47) == 0) {  // lanes 0 and 16: chains (0, 1) and (2, 3)
-          if (vA) {
-            A.pack[iA * 4 + 2] = refA;
-            if (t == 0) A.pack[iA * 4 + 3] = 1.f;
-            if (t + 1 < L) A.pack[(iA + 1) * 4 + 3] = sA;
-          }
-          if (vB) {
-            A.pack[iB * 4 + 2] = refB;
-            if (t == 0) A.pack[iB * 4 + 3] = 1.f;
-            if (t + 1 < L) A.pack[(iB + 1) * 4 + 3] = sB;
-          }
+        const float wn = scb[0];  // w_{t+1}
+        float a[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          a[e] = (j > 0 ? o[e] * sc_prev : 1.f) * ex2(ell[e] - ref);
+          xw[4 * e] = a[e];
+          if (valid) A.ha[i0 + 16 * e] = a[e];
+          const float d = wn - cc[e];
+          nl[e] = ck[e] - kap * d * d;
         }
-        ellA = nA;
-        ellB = nB;
-        refA = out[1][0];
-        refB = out[1][1];
+        const float v[2] = {a[0] + a[1], fmaxf(nl[0], nl[1])};
+        publish<2, 2, C::NW>(v, red[buf], l, wv);
       } else if constexpr (MODE == kBeta) {
-        const float uA = j > 0 ? o0 * sA : 1.f;
-        const float uB = j > 0 ? o1 * sB : 1.f;
-        const float aA = ra[0], aB = ra[1];
-        if (vA) A.hb[iA * S + col] = uA;
-        if (vB) A.hb[iB * S + col] = uB;
-        if (t > 0) {
-          const f2 wt = *reinterpret_cast<const f2*>(scb);
-          const f2 rf = *reinterpret_cast<const f2*>(scb + 4);
-          const float dA = wt[0] - cc, dB = wt[1] - cc;
-          xw[0] = ex2(cmk - kap * dA * dA - rf[0]) * uA;
-          xw[C::XSTR] = ex2(cmk - kap * dB * dB - rf[1]) * uB;
-        }
-        const float pA = aA * uA, pB = aB * uB;
-        const float v[2][2] = {{pA, pB}, {cc * pA, cc * pB}};
-        float out[2][2];
-        if (last) stage_store((int)((cidx + 1) & 1));
-        chain_reduce<2, 0, C::NW>(v, red[buf], l, wv, out);
-        if (tt == 0 && cidx + 1 < nch) stage_load(cidx + 1);
-        sA = 1.f / out[0][0];
-        sB = 1.f / out[0][1];
-        if (wv == 0 && (l & 47) == 0) {
-          if (vA) {
-            const float wh = out[1][0] / out[0][0];
-            A.pack[iA * 4 + 0] = wh;
-            A.pack[iA * 4 + 1] = sA;
-            A.w_hat[iA] = wh;
+        const float wt = scb[0], rf = scb[4];
+        float p[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float u = j > 0 ? o[e] * sc_prev : 1.f;
+          if (valid) A.hb[i0 + 16 * e] = u;
+          if (t > 0) {
+            const float d = wt - cc[e];
+            xw[4 * e] = ex2(ck[e] - kap * d * d - rf) * u;
           }
-          if (vB) {
-            const float wh = out[1][1] / out[0][1];
-            A.pack[iB * 4 + 0] = wh;
-            A.pack[iB * 4 + 1] = sB;
-            A.w_hat[iB] = wh;
-          }
+          p[e] = ra[e] * u;
         }
+        const float v[2] = {p[0] + p[1], cc[0] * p[0] + cc[1] * p[1]};
+        publish<2, 0, C::NW>(v, red[buf], l, wv);
       } else if constexpr (MODE == kPsi) {
-        const f2 wt = *reinterpret_cast<const f2*>(scb);
-        const f2 gt = *reinterpret_cast<const f2*>(scb + 4);
-        const f2 wh = *reinterpret_cast<const f2*>(scb + 8);
-        const f2 rz = *reinterpret_cast<const f2*>(scb + 12);
-        const f2 rf = *reinterpret_cast<const f2*>(scb + 16);
-        const f2 inv = *reinterpret_cast<const f2*>(scb + 20);
-        const float vvA = j > 0 ? o0 * sA : 0.f, vvB = j > 0 ? o1 * sB : 0.f;
-        const float aA = ra[0], aB = ra[1], uA = rb[0], uB = rb[1];
-        const float buA = uA * (gt[0] * (cc - wh[0])) + vvA;
-        const float buB = uB * (gt[1] * (cc - wh[1])) + vvB;
-        const float DA = aA * buA * rz[0], DB = aB * buB * rz[1];
-        const float gmA = aA * uA * rz[0], gmB = aB * uB * rz[1];
-        gc += fA * (gt[0] * gmA + A.two_t * (wt[0] - cc) * (DA + hA * gmA));
-        gc += fB * (gt[1] * gmB + A.two_t * (wt[1] - cc) * (DB + hB * gmB));
-        if (t > 0) {
-          const float dA = wt[0] - cc, dB = wt[1] - cc;
-          const float eA = ex2(cmk - kap * dA * dA - rf[0]);
-          const float eB = ex2(cmk - kap * dB * dB - rf[1]);
-          const float zA = eA * buA, zB = eB * buB;
-          xw[0] = zA;
-          xw[C::XSTR] = zB;
-          const float qA = inv[0] * rz[0], qB = inv[1] * rz[1];
-          if (vA) {
-            A.r1[iA * S + col] = eA * uA * qA;
-            A.r2[iA * S + col] = zA * qA;
-          }
-          if (vB) {
-            A.r1[iB * S + col] = eB * uB * qB;
-            A.r2[iB * S + col] = zB * qB;
+        const float wt = scb[0], gt = scb[4], wh = scb[8], rz = scb[12], rf = scb[16], inv = scb[20];
+        float D[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float a = ra[e], u = rb[e];
+          const float bu = u * (gt * (cc[e] - wh)) + (j > 0 ? o[e] * sc_prev : 0.f);
+          D[e] = a * bu * rz;
+          const float gm = a * u * rz;
+          gc[e] += fv * (gt * gm + A.two_t * (wt - cc[e]) * (D[e] + hh * gm));
+          if (t > 0) {
+            const float d = wt - cc[e];
+            const float ee = ex2(ck[e] - kap * d * d - rf);
+            const float z = ee * bu;
+            xw[4 * e] = z;
+            const float q = inv * rz;
+            if (valid) {
+              A.r1[i0 + 16 * e] = ee * u * q;
+              A.r2[i0 + 16 * e] = z * q;
+            }
           }
         }
-        const float v[1][2] = {{cc * DA, cc * DB}};
-        float out[1][2];
-        if (last) stage_store((int)((cidx + 1) & 1));
-        chain_reduce<1, 0, C::NW>(v, red[buf], l, wv, out);
-        if (tt == 0 && cidx + 1 < nch) stage_load(cidx + 1);
-        sA = rz[0];
-        sB = rz[1];
-        if (wv == 0 && (l & 47) == 0) {
-          if (vA) A.grad_w[iA] = A.two_t * (out[0][0] + hA * (wh[0] - wt[0]));
-          if (vB) A.grad_w[iB] = A.two_t * (out[0][1] + hB * (wh[1] - wt[1]));
-        }
+        const float v[1] = {cc[0] * D[0] + cc[1] * D[1]};
+        publish<1, 0, C::NW>(v, red[buf], l, wv);
+        sc_prev = rz;
+        p_wh = wh;
+        p_wt = wt;
       } else {  // kPhi
-        const f2 wt = *reinterpret_cast<const f2*>(scb);
-        const f2 gt = *reinterpret_cast<const f2*>(scb + 4);
-        const f2 wh = *reinterpret_cast<const f2*>(scb + 8);
-        const f2 rz = *reinterpret_cast<const f2*>(scb + 12);
-        const f2 rf = *reinterpret_cast<const f2*>(scb + 16);
-        const f2 inv = *reinterpret_cast<const f2*>(scb + 20);
-        float atA = 0.f, atB = 0.f;
-        if (j > 0) {
-          const float dA = wt[0] - cc, dB = wt[1] - cc;
-          atA = o0 * inv[0] * ex2(cmk - kap * dA * dA - rf[0]);
-          atB = o1 * inv[1] * ex2(cmk - kap * dB * dB - rf[1]);
+        const float wt = scb[0], gt = scb[4], wh = scb[8], rz = scb[12], rf = scb[16], inv = scb[20];
+        float D[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float at = 0.f;
+          if (j > 0) {
+            const float d = wt - cc[e];
+            at = o[e] * inv * ex2(ck[e] - kap * d * d - rf);
+          }
+          const float a = ra[e], u = rb[e];
+          D[e] = at * u * rz;
+          gc[e] += fv * (A.two_t * (wt - cc[e]) * D[e]);
+          if (t + 1 < L) {
+            const float x = at + a * (gt * (cc[e] - wh));
+            xw[4 * e] = x;
+            if (valid) A.l1[i0 + 16 * e] = x + hh * a;
+          }
         }
-        const float aA = ra[0], aB = ra[1], uA = rb[0], uB = rb[1];
-        const float DA = atA * uA * rz[0], DB = atB * uB * rz[1];
-        gc += fA * (A.two_t * (wt[0] - cc) * DA);
-        gc += fB * (A.two_t * (wt[1] - cc) * DB);
-        if (t + 1 < L) {
-          const float xA = atA + aA * (gt[0] * (cc - wh[0]));
-          const float xB = atB + aB * (gt[1] * (cc - wh[1]));
-          xw[0] = xA;
-          xw[C::XSTR] = xB;
-          if (vA) A.l1[iA * S + col] = xA + hA * aA;
-          if (vB) A.l1[iB * S + col] = xB + hB * aB;
-        }
-        const float v[1][2] = {{cc * DA, cc * DB}};
-        float out[1][2];
-        if (last) stage_store((int)((cidx + 1) & 1));
-        chain_reduce<1, 0, C::NW>(v, red[buf], l, wv, out);
-        if (tt == 0 && cidx + 1 < nch) stage_load(cidx + 1);
-        if (wv == 0 && (l & 47) == 0) {
-          if (vA) A.grad_w[iA] += A.two_t * out[0][0];
-          if (vB) A.grad_w[iB] += A.two_t * out[0][1];
-        }
+        const float v[1] = {cc[0] * D[0] + cc[1] * D[1]};
+        publish<1, 0, C::NW>(v, red[buf], l, wv);
       }
+      if (tt == kChunk - 1 && cidx + 1 < nch) stage_store((int)((cidx + 1) & 1));
+      __syncthreads();
+      if (tt == 0 && cidx + 1 < nch) stage_load(cidx + 1);
       hist_load(j + 2, ra, rb);
     };
 
@@ -492,41 +462,51 @@ k_dense_sweep(SweepArgs A) {
       step(j, ra0, rb0);
       if (j + 1 < L) step(j + 1, ra1, rb1);
     }
-    if (MODE == kAlpha && wv == 0 && (l & 47) == 0) {
-      if (vA) {
-        A.lz2[bA] = lzA;
-        A.log_z[bA] = (float)(lzA * kLn2D);
-      }
-      if (vB) {
-        A.lz2[bB] = lzB;
-        A.log_z[bB] = (float)(lzB * kLn2D);
-      }
+    finish(L - 1);
+    if (MODE == kAlpha && wv == 0 && (l & 15) == 0 && valid) {
+      A.lz2[b] = lz;
+      A.log_z[b] = (float)(lz * kLn2D);
     }
   }
   if (MODE == kPsi || MODE == kPhi) {
-    // lanes l and l ^ 16 hold the same state (chains 0, 1 and 2, 3)
-    const P2 r = swap16(gc, gc);
-    if (((l >> 4) & 1) == 0) A.gc_part[(long long)blockIdx.x * S + col] = r.lo + r.hi;
+    // sum the four chains (rows) of every state
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const P2 r = swap32(gc[e], gc[e]);
+      const float x = r.lo + r.hi;
+      const P2 q = swap16(x, x);
+      if (l < 16) A.gc_part[(long long)blockIdx.x * S + col0 + 16 * e] = q.lo + q.hi;
+    }
   }
 }
 
-// M = 2^(kappa (theta - cm)), kappa cm; one thread per column s'.
+// Column maxima cm(s') of theta, M = 2^(kappa (theta - cm)) and kappa cm. One block per column.
 __global__ void __launch_bounds__(256)
 k_dense_prep(const float* __restrict__ theta, int S, float kap, float* __restrict__ mat,
              float* __restrict__ cmk) {
-  const int sp = threadIdx.x;
-  if (sp >= S) return;
-  float cm = theta[sp];
-  for (int s = 1; s < S; ++s) cm = fmaxf(cm, theta[s * S + sp]);
-  for (int s = 0; s < S; ++s) mat[s * S + sp] = ex2(kap * (theta[s * S + sp] - cm));
-  cmk[sp] = kap * cm;
+  __shared__ float red[4];
+  const int sp = blockIdx.x, s = threadIdx.x;
+  const float th = s < S ? theta[s * S + sp] : -INFINITY;
+  float m = th;
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 8, 64));
+  m = fmaxf(m, __shfl_xor(m, 4, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  if ((s & 63) == 0) red[s >> 6] = m;
+  __syncthreads();
+  const float cm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (s < S) mat[s * S + sp] = ex2(kap * (th - cm));
+  if (s == 0) cmk[sp] = kap * cm;
 }
 
 // ---- theta gradient: G = sum over (chain, t >= 1) of L1_{t-1} (x) R1_t + a_{t-1} (x) R2_t ----
 // Split-K over all (chain, step) pairs: block j sums a contiguous range of 8-pair chunks into a
 // full S x S partial. A chunk is 16 rows (pair p, term) of left and right vectors, staged in LDS
 // as [state][row % 4][row / 4] (row stride 20 floats) so that one 16-byte read gives the four
-// k-steps of an MFMA 16x16x4 operand.
+// k-steps of an MFMA 16x16x4 operand. Loader lanes take the 16 rows of one group of 4 states in
+// turn, so that their transposing LDS stores fall into distinct banks.
 template <int S_>
 struct GGeo {
   static constexpr int S = S_;
@@ -568,7 +548,7 @@ k_dense_theta_gemm(GemmArgs A) {
       const int idx = tid + p * G::BLOCK;
       vl[p] = vr[p] = f4{0.f, 0.f, 0.f, 0.f};
       if (idx < 16 * S / 4) {
-        const int kr = idx / (S / 4), s = 4 * (idx % (S / 4));
+        const int kr = idx & 15, s = 4 * (idx >> 4);
         const long long pr = c * G::PC + (kr >> 1);
         if (pr < A.pairs) {
           const long long b = pr / Lm1, t = 1 + pr % Lm1;
@@ -586,7 +566,7 @@ k_dense_theta_gemm(GemmArgs A) {
     for (int p = 0; p < G::NI; ++p) {
       const int idx = tid + p * G::BLOCK;
       if (idx < 16 * S / 4) {
-        const int kr = idx / (S / 4), s = 4 * (idx % (S / 4));
+        const int kr = idx & 15, s = 4 * (idx >> 4);
         const int off = (kr & 3) * 4 + (kr >> 2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -637,22 +617,33 @@ k_dense_theta_gemm(GemmArgs A) {
         out[(sb + 16 * i + 4 * (l >> 4) + r) * S + sbp + 16 * k + (l & 15)] = acc[i][k][r];
 }
 
-// grad_theta = (M / T) o sum_j part_j; grad_c = sum of the two sweeps' partials (fixed order).
+// out[e] = scale * mul[e] * sum_j part[j * n + e] (mul may be null), summed over j in a fixed
+// order: four contiguous quarters of j, each in order, then the quarters in order. A block
+// covers 64 consecutive e.
 __global__ void __launch_bounds__(256)
-k_dense_finalize(const float* __restrict__ gpart, int ngrid, const float* __restrict__ mat,
-                 float inv_t, float* __restrict__ grad_theta, const float* __restrict__ gcpart,
-                 int ngc, float* __restrict__ grad_c, int S) {
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long SS = (long long)S * S;
-  if (e < SS) {
-    float acc = 0.f;
-    for (int j = 0; j < ngrid; ++j) acc += gpart[j * SS + e];
-    grad_theta[e] = inv_t * mat[e] * acc;
-  } else if (e < SS + S) {
-    const long long s = e - SS;
-    float acc = 0.f;
-    for (int j = 0; j < ngc; ++j) acc += gcpart[j * (long long)S + s];
-    grad_c[s] = acc;
+k_dense_sum_parts(const float* __restrict__ part, int np, long long n, const float* __restrict__ mul,
+                  float scale, float* __restrict__ out) {
+  __shared__ float red[4][64];
+  const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const long long e = (long long)blockIdx.x * 64 + el;
+  float acc = 0.f;
+  if (e < n) {
+    const int j0 = np * q / 4, j1 = np * (q + 1) / 4;
+    int j = j0;
+    for (; j + 8 <= j1; j += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(long long)(j + u) * n + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; j < j1; ++j) acc += part[(long long)j * n + e];
+  }
+  red[q][el] = acc;
+  __syncthreads();
+  if (q == 0 && e < n) {
+    const float tot = ((red[0][el] + red[1][el]) + red[2][el]) + red[3][el];
+    out[e] = mul != nullptr ? scale * mul[e] * tot : tot;
   }
 }
 
@@ -696,7 +687,7 @@ int run_forward(const float* theta, const float* cb, const float* w, int64_t B, 
   a.hb = reinterpret_cast<float*>(sv + d.hb);
   const int ga = sweep_grid<S, kAlpha>(a.units), gb = sweep_grid<S, kBeta>(a.units);
   if (ga <= 0 || gb <= 0) return (int)hipErrorInvalidDevice;
-  hipLaunchKernelGGL(k_dense_prep, dim3(1), dim3(256), 0, st, theta, S, kap, mat, cmk);
+  hipLaunchKernelGGL(k_dense_prep, dim3(S), dim3(256), 0, st, theta, S, kap, mat, cmk);
   int e = (int)hipGetLastError();
   if (e) return e;
   if ((e = run_sweep<S, kAlpha>(a, ga, st))) return e;
@@ -752,7 +743,7 @@ int run_backward(const float* theta, const float* cb, const float* w, int64_t B,
   if (gpsi <= 0 || gphi <= 0 || gg <= 0) return (int)hipErrorInvalidDevice;
   if (ga.chunks > 0 && gg > ga.chunks) gg = (int)ga.chunks;
 
-  hipLaunchKernelGGL(k_dense_prep, dim3(1), dim3(256), 0, st, theta, S, kap, mat, cmk);
+  hipLaunchKernelGGL(k_dense_prep, dim3(S), dim3(256), 0, st, theta, S, kap, mat, cmk);
   int e = (int)hipGetLastError();
   if (e) return e;
   a.gc_part = gcp;
@@ -761,9 +752,12 @@ int run_backward(const float* theta, const float* cb, const float* w, int64_t B,
   if ((e = run_sweep<S, kPhi>(a, gphi, st))) return e;
   hipLaunchKernelGGL(k_dense_theta_gemm<S>, dim3(gg), dim3(G::BLOCK), 0, st, ga);
   if ((e = (int)hipGetLastError())) return e;
-  const long long n = (long long)S * S + S;
-  hipLaunchKernelGGL(k_dense_finalize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ga.part,
-                     gg, mat, 1.f / T, grad_theta, gcp, gpsi + gphi, grad_c, S);
+  const long long nt = (long long)S * S;
+  hipLaunchKernelGGL(k_dense_sum_parts, dim3((unsigned)((nt + 63) / 64)), dim3(256), 0, st, ga.part,
+                     gg, nt, mat, 1.f / T, grad_theta);
+  if ((e = (int)hipGetLastError())) return e;
+  hipLaunchKernelGGL(k_dense_sum_parts, dim3((unsigned)((S + 63) / 64)), dim3(256), 0, st, gcp,
+                     gpsi + gphi, (long long)S, nullptr, 1.f, grad_c);
   return (int)hipGetLastError();
 }
 

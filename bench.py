@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--temp", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1536, help="chains timed on the CPU oracle")
+    ap.add_argument("--cpu-sample-dense", type=int, default=64,
+                    help="chains of the dense workload timed on the CPU oracle")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -127,6 +129,119 @@ def cpu_baseline(wl, c, w, g, T, sample):
     }
 
 
+# ---------------------------------------------------------------------------------------------
+# Dense trellis (fully connected, S x S transition matrix): algorithmic matrix-core work per
+# state-step, counted from the recursions (a multiply-add is 2 flops):
+#   forward call : alpha sweep S MACs + beta sweep S MACs                       -> 4 S flops
+#   backward call: Psi sweep S MACs + Phi sweep S MACs + theta gradient 2 S MACs -> 8 S flops
+#                  (the theta gradient runs over the L-1 transitions of a chain)
+# Peak: dense fp32 MFMA, 157.3 TFLOP/s on MI355X.
+# ---------------------------------------------------------------------------------------------
+PEAK_FP32_MFMA = 157.3
+
+
+def dense_flops(B, L, S):
+    fwd = 2.0 * (2 * S) * B * L * S
+    bwd = 2.0 * (2 * S) * B * L * S + 2.0 * (2 * S) * B * (L - 1) * S
+    return fwd, bwd
+
+
+def cpu_baseline_dense(wl, th, c, w, g, T, sample):
+    import oracle
+    cores = oracle.set_threads(0)
+    t0 = time.perf_counter()
+    oracle.dense_forward(th, c, w[:sample], T)
+    oracle.dense_backward(th, c, w[:sample], T, g[:sample])
+    dt = time.perf_counter() - t0
+    return {
+        "value": sample * wl.L * wl.S / dt,
+        "unit": "state-steps/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"first {sample} of {wl.B} chains (L={wl.L}, S={wl.S} dense), fp64 oracle "
+                  f"forward + backward incl. theta gradient, {dt:.1f} s on {cores} OpenMP threads",
+    }
+
+
+def bench_dense(args, wl):
+    import numpy as np
+    import torch
+
+    from bcjr_soft_decoding_amd import bcjr, synth
+    T = args.temp if args.temp is not None else wl.temps[0]
+    B, L, S = wl.B, wl.L, wl.S
+    i = wl.index
+    th_np, c_np, w_np, g_np = synth.theta(i), synth.codebook(i), synth.weights(i), synth.upstream_grad(i)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    th, c, w, g = (torch.from_numpy(a).to(dev) for a in (th_np, c_np, w_np, g_np))
+    w_hat = torch.empty_like(w)
+    log_z = torch.empty(B, dtype=torch.float32, device=dev)
+    saved = torch.empty(bcjr.bcjr_dense_saved_bytes(S, B, L), dtype=torch.uint8, device=dev)
+    grad_w = torch.empty_like(w)
+    grad_c = torch.empty_like(c)
+    grad_th = torch.empty_like(th)
+    wsf = bcjr.dense_workspace(S, B, L, bcjr.FWD, dev)
+    wsb = bcjr.dense_workspace(S, B, L, bcjr.BWD, dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bcjr.bcjr_dense_forward(th, c, w, T, w_hat, log_z, saved, wsf)
+        if ev is not None:
+            ev[1].record()
+        bcjr.bcjr_dense_backward(th, c, w, T, saved, g, None, grad_w, grad_c, grad_th, wsb)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    assert torch.isfinite(w_hat).all() and torch.isfinite(grad_th).all()
+    ff, fb = dense_flops(B, L, S)
+    achieved = fb / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": B * L * S / (elapsed / args.steps),
+        "unit": "state-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "L": L, "S": S, "T": T, "trellis": "dense",
+                   "parallelism": "single-gpu"},
+        "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bcjr_dense_backward (k_dense_sweep Psi + Phi, k_dense_theta_gemm)",
+            "achieved": achieved,
+            "peak": PEAK_FP32_MFMA,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_MFMA,
+            "flops_per_launch": fb,
+            "forward_frac": ff / (fwd_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_dense(wl, th_np, c_np, w_np, g_np, T,
+                                                 min(args.cpu_sample_dense, B))
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -145,7 +260,7 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     if wl.dense:
-        raise SystemExit("the dense workload is not part of this benchmark")
+        return bench_dense(args, wl)
     T = args.temp if args.temp is not None else wl.temps[0]
     n, k, B, L, S = wl.n, wl.k, wl.B, wl.L, wl.S
     c_np, w_np, g_np = synth.codebook(args.workload), synth.weights(args.workload), synth.upstream_grad(args.workload)
