@@ -6,4 +6,4 @@ The work is done by hand-written HIP kernels behind the C ABI declared in ``incl
 The library is loaded on first use, and a missing library is an error, never a fallback.
 """
 
-__all__ = ["bcjr", "synth"]
+__all__ = ["autograd", "bcjr", "synth"]

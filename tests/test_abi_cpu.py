@@ -181,3 +181,14 @@ def test_dense_rejects_bad_arguments_without_device(lib):
     assert bwd(S=100) == bcjr.BCJR_E_UNSUPPORTED
     need = bcjr.bcjr_dense_workspace_bytes(64, 4, 8, 1)
     assert bwd(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
+
+
+def test_autograd_wrapper_refuses_cpu_tensors():
+    import torch
+    from bcjr_soft_decoding_amd import autograd
+    w = torch.zeros((2, 8), dtype=torch.float32)
+    c = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        autograd.soft_quantize(w, c, 4, 2, 0.5)
+    with pytest.raises(ValueError):
+        autograd.dense_soft_quantize(w, torch.zeros(32), torch.zeros((32, 32)), 0.5)
