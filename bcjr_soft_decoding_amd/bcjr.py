@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BCJR_LIB", os.path.join(_PKG, "_lib", "libbcjr.so"))
 
 BCJR_OK, BCJR_E_ARG, BCJR_E_SHAPE, BCJR_E_WORKSPACE, BCJR_E_DEVICE, BCJR_E_UNSUPPORTED = range(6)
-FWD, BWD, VIT = 0, 1, 2
+FWD, BWD, VIT, FWD_CKPT, BWD_CKPT = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "bcjr_supported", "bcjr_saved_bytes", "bcjr_workspace_bytes", "bcjr_forward",

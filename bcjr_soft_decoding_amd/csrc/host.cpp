@@ -40,11 +40,12 @@ int resident_grid(const void* kernel, int block, int64_t slots) {
   return (int)(slots < cap ? slots : cap);
 }
 
-size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L) {
-  return (size_t)g.slots * sparse_fwd_slot_bytes(g, L);
+size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+  return (size_t)g.slots * sparse_fwd_slot_bytes(g, L, ckpt);
 }
-size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L) {
-  return (size_t)g.slots * sparse_bwd_slot_bytes(g, L) + round256((size_t)g.slots * g.S * sizeof(float));
+size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+  return (size_t)g.slots * sparse_bwd_slot_bytes(g, L, ckpt) +
+         round256((size_t)g.slots * g.S * sizeof(float));
 }
 size_t sparse_vit_ws_bytes(const SparseGeom& g, int64_t L) {
   return round256((size_t)g.slots * L * g.BLOCK * (g.K * g.G));
@@ -78,6 +79,20 @@ bool ws_ok(const void* ws, size_t have, size_t need) {
   return ws != nullptr && have >= need && ((uintptr_t)ws & 15) == 0;
 }
 
+// History layout from the workspace the caller passed: the full history when it fits, else the
+// checkpointed one, else an error.
+bcjr_status pick_layout(const void* ws, size_t have, size_t need_full, size_t need_ckpt, bool* ckpt) {
+  if (ws_ok(ws, have, need_full)) {
+    *ckpt = false;
+    return BCJR_OK;
+  }
+  if (ws_ok(ws, have, need_ckpt)) {
+    *ckpt = true;
+    return BCJR_OK;
+  }
+  return BCJR_E_WORKSPACE;
+}
+
 bcjr_status from_hip(int e) { return e == 0 ? BCJR_OK : BCJR_E_DEVICE; }
 
 // Dense shapes: S >= 1, B >= 0, L >= 1, and every [B, L, S] array addressable with 64-bit
@@ -106,14 +121,17 @@ size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L) {
 
 size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int which) {
   if (tr == nullptr || !shape_ok(tr) || B < 0 || L < 1 || tr->weights_per_step != 1) return 0;
-  if (which < 0 || which > 2) return 0;
+  if (which < 0 || which > 4) return 0;
+  const int kind = which == 3 ? kFwd : which == 4 ? kBwd : which;
   SparseGeom g;
-  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, which, &g)) return 0;
+  if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, kind, &g)) return 0;
   if (B == 0) return 0;
   switch (which) {
-    case 0: return sparse_fwd_ws_bytes(g, L);
-    case 1: return sparse_bwd_ws_bytes(g, L);
+    case 0: return sparse_fwd_ws_bytes(g, L, false);
+    case 1: return sparse_bwd_ws_bytes(g, L, false);
     case 2: return sparse_vit_ws_bytes(g, L);
+    case 3: return sparse_fwd_ws_bytes(g, L, true);
+    case 4: return sparse_bwd_ws_bytes(g, L, true);
     default: return 0;
   }
 }
@@ -127,10 +145,12 @@ bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int6
   if (!temp_ok(T)) return BCJR_E_ARG;
   if (B == 0) return BCJR_OK;
   if (!w || !w_hat || !log_z || !saved) return BCJR_E_ARG;
-  const size_t need = sparse_fwd_ws_bytes(g, L);
-  if (!ws_ok(ws, ws_bytes, need)) return BCJR_E_WORKSPACE;
+  bool ckpt = false;
+  st = pick_layout(ws, ws_bytes, sparse_fwd_ws_bytes(g, L, false), sparse_fwd_ws_bytes(g, L, true),
+                   &ckpt);
+  if (st != BCJR_OK) return st;
   return from_hip(launch_sparse_forward(g, tr->codebook, w, B, L, T, w_hat, log_z,
-                                        static_cast<float*>(saved), ws, stream));
+                                        static_cast<float*>(saved), ws, ckpt, stream));
 }
 
 bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
@@ -147,11 +167,13 @@ bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int
     return from_hip(launch_fill_zero(grad_codebook, (int64_t)1 << tr->state_bits, stream));
   }
   if (!w || !saved || !grad_w_hat || !grad_w) return BCJR_E_ARG;
-  const size_t need = sparse_bwd_ws_bytes(g, L);
-  if (!ws_ok(ws, ws_bytes, need)) return BCJR_E_WORKSPACE;
+  bool ckpt = false;
+  st = pick_layout(ws, ws_bytes, sparse_bwd_ws_bytes(g, L, false), sparse_bwd_ws_bytes(g, L, true),
+                   &ckpt);
+  if (st != BCJR_OK) return st;
   return from_hip(launch_sparse_backward(g, tr->codebook, w, B, L, T,
                                          static_cast<const float*>(saved), grad_w_hat, grad_log_z,
-                                         grad_w, grad_codebook, ws, stream));
+                                         grad_w, grad_codebook, ws, ckpt, stream));
 }
 
 bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host layer (host.cpp) and the kernel files (*.hip).
 // Nothing here is part of the public ABI (include/bcjr.h).
 #pragma once
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -42,28 +43,46 @@ inline size_t saved_bytes(int64_t B, int64_t L) {
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout of the sparse kernels: one slot per persistent block. A forward slot holds
-// the lam history [L][BLOCK][K*G] with 8-byte entries and the shift prefix [L][SPB] (double);
-// a backward slot adds the Phi history [L][BLOCK][K*G] (fp32); the backward workspace ends
+// the lam history [H][BLOCK][K*G] with 8-byte entries and the shift prefix [L][SPB] (double);
+// a backward slot adds the Phi history [H][BLOCK][K*G] (fp32); the backward workspace ends
 // with the codebook-gradient partials [slots][S] (fp32). Sizes do not depend on T.
-inline size_t sparse_fwd_slot_bytes(const SparseGeom& g, int64_t L) {
-  return round256((size_t)L * g.BLOCK * (g.K * g.G) * 8 + (size_t)L * g.SPB * 8);
+// Full history: H = L entries, one per step. Checkpointed history: every C-th step is kept
+// (C = ceil(sqrt(L))) and the reverse sweep recomputes one segment of C steps at a time into a
+// C-entry buffer, so H = ceil(L / C) + C (about 2 sqrt(L)) at the cost of one more forward
+// recursion.
+inline int64_t sparse_seg_len(int64_t L) {
+  int64_t c = (int64_t)sqrt((double)L);
+  while (c * c < L) ++c;
+  while (c > 1 && (c - 1) * (c - 1) >= L) --c;
+  return c < 1 ? 1 : c;
 }
-inline size_t sparse_bwd_slot_bytes(const SparseGeom& g, int64_t L) {
-  return round256((size_t)L * g.BLOCK * (g.K * g.G) * 12 + (size_t)L * g.SPB * 8);
+inline int64_t sparse_hist_entries(int64_t L, bool ckpt) {
+  if (!ckpt) return L;
+  const int64_t c = sparse_seg_len(L);
+  return (L + c - 1) / c + c;
 }
-size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L);
-size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L);
+inline size_t sparse_fwd_slot_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+  return round256((size_t)sparse_hist_entries(L, ckpt) * g.BLOCK * (g.K * g.G) * 8 +
+                  (size_t)L * g.SPB * 8);
+}
+inline size_t sparse_bwd_slot_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+  return round256((size_t)sparse_hist_entries(L, ckpt) * g.BLOCK * (g.K * g.G) * 12 +
+                  (size_t)L * g.SPB * 8);
+}
+size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt);
+size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt);
 size_t sparse_vit_ws_bytes(const SparseGeom& g, int64_t L);
 
 // Kernel launchers (defined in sparse_kernels.hip / viterbi_kernels.hip). They assume every
 // argument was validated by the host layer. Return a hipError_t as int.
+// ckpt selects the checkpointed history layout (see sparse_hist_entries).
 int launch_sparse_forward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                           int64_t L, float T, float* w_hat, float* log_z, float* saved_logz2,
-                          void* ws, void* stream);
+                          void* ws, bool ckpt, void* stream);
 int launch_sparse_backward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                            int64_t L, float T, const float* saved_logz2, const float* grad_w_hat,
                            const float* grad_log_z, float* grad_w, float* grad_codebook, void* ws,
-                           void* stream);
+                           bool ckpt, void* stream);
 int launch_fill_zero(float* dst, int64_t count, void* stream);
 // Grid of a persistent kernel: min(slots, resident blocks on the current device), or -1.
 int resident_grid(const void* kernel, int block, int64_t slots);

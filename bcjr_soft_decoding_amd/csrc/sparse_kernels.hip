@@ -42,6 +42,11 @@
 #include "geom.h"
 #include "internal.h"
 
+// Multiply-adds are fused only within one expression (or explicitly with __builtin_fmaf), never
+// across statements: the forward step is inlined twice (the sweep and, with checkpoints, the
+// segment replay), and both copies must round identically.
+#pragma clang fp contract(on)
+
 namespace bcjr {
 namespace {
 
@@ -257,12 +262,12 @@ struct CodebookLane<C, true> {
 // ---------------------------------------------------------------------------------------------
 // Forward: soft codeword and log Z.
 // ---------------------------------------------------------------------------------------------
-template <class C>
+template <class C, bool CK>
 __global__ void __launch_bounds__(C::BLOCK)
 k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long long B, long long L,
              Consts k, float* __restrict__ w_hat, float* __restrict__ log_z,
              double* __restrict__ saved_lz, float* __restrict__ saved_what, void* __restrict__ ws,
-             size_t slot_bytes, long long units) {
+             size_t slot_bytes, long long units, long long seg_arg) {
   using P = typename C::P;
   using MT = typename C::MT;
   constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
@@ -277,10 +282,17 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
   CodebookLane<C> vsrc;
   vsrc.init(cb, k.sc, p);
 
-  // slot layout: lam history [L][BLOCK][KG] (8-byte entries), shift prefix N [L][SPB] (double)
+  // slot layout: lam history [H][BLOCK][KG] (8-byte entries), shift prefix N [L][SPB] (double).
+  // Full history (CK false): H = L, entry t is step t. Checkpointed (CK, seg = C): entries
+  // 0 .. ncp-1 are the checkpoints of steps 0, C, 2C, ..., entries ncp .. ncp+C-1 the segment
+  // being replayed.
+  const long long seg = CK ? seg_arg : 0;
+  const long long ncp = seg ? (L + seg - 1) / seg : L;
+  const long long nh = seg ? ncp + seg : L;
   char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
   MT* __restrict__ hs = reinterpret_cast<MT*>(sb);
-  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)L * BLOCK * KG * 8);
+  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * BLOCK * KG * 8);
+  auto hist = [&](long long e) { return hs + ((size_t)e * BLOCK + tid) * KG; };
   int mb = 0, rp = 0;
 
   for (long long unit = blockIdx.x; unit < units; unit += gridDim.x) {
@@ -288,16 +300,15 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
     const bool valid = b < B;
     const float* __restrict__ wb = w + (valid ? b : B - 1) * L;
 
-    // ---- phase A: forward messages lam, t = 0 .. L-1 -------------------------------------
     MT lc[G][K];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int a = 0; a < K; ++a) lc[g][a] = (MT)0;
     double N = 0.0, lz2 = 0.0;
-    for (long long t = 0; t < L; ++t) {
-      store_vec<KG>(hs + ((size_t)t * BLOCK + tid) * KG, &lc[0][0]);
-      if (p == 0) ns[t * SPB + q] = N;
+
+    // One forward step: the column offsets lc of step t -> those of step t + 1 (t < L - 1).
+    auto advance = [&](long long t) {
       const float u = k.sc * wb[t];
       MT out[G][K];
       MT mx = (MT)-INFINITY;
@@ -321,19 +332,6 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           mx = tmax(mx, out[g][r]);
         }
       }
-      if (t == L - 1) {
-        MT v1[1] = {mx};
-        chain_reduce<C, 1, 1u>(v1, red, rp);
-        float s2 = 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int r = 0; r < K; ++r) s2 += ex2((float)(out[g][r] - v1[0]));  // once per chain
-        float v2[1] = {s2};
-        chain_reduce<C, 1, 0u>(v2, red, rp);
-        lz2 = N + ((double)v1[0] + (double)lg2(v2[0]));
-        break;
-      }
       MT* mw = msg[mb] + q * M;
 #pragma unroll
       for (int g = 0; g < G; ++g) store_vec<K>(mw + K * (p + g * LPS), out[g]);
@@ -346,88 +344,146 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int a = 0; a < K; ++a) lc[g][a] = mw[p + g * LPS + a * NG] - sh;
       N += (double)sh;
       if constexpr (C::DB) mb ^= 1; else __syncthreads();
+    };
+
+    // ---- phase A: forward messages lam, t = 0 .. L-1 -------------------------------------
+    for (long long t = 0; t < L; ++t) {
+      if (seg == 0 || t % seg == 0) store_vec<KG>(hist(seg ? t / seg : t), &lc[0][0]);
+      if (p == 0) ns[t * SPB + q] = N;
+      if (t == L - 1) {
+        const float u = k.sc * wb[t];
+        MT out[G][K];
+        MT mx = (MT)-INFINITY;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float Vg[K][K];
+          vsrc.get(g, Vg);
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            MT x[K];
+            MT m = (MT)-INFINITY;
+#pragma unroll
+            for (int a = 0; a < K; ++a) {
+              x[a] = emit<P>(u, Vg[r][a], lc[g][a], k.kap);
+              m = tmax(m, x[a]);
+            }
+            float s = ex2((float)(x[0] - m));
+#pragma unroll
+            for (int a = 1; a < K; ++a) s += ex2((float)(x[a] - m));
+            out[g][r] = m + (MT)lg2(s);
+            mx = tmax(mx, out[g][r]);
+          }
+        }
+        MT v1[1] = {mx};
+        chain_reduce<C, 1, 1u>(v1, red, rp);
+        float s2 = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < K; ++r) s2 += ex2((float)(out[g][r] - v1[0]));  // once per chain
+        float v2[1] = {s2};
+        chain_reduce<C, 1, 0u>(v2, red, rp);
+        lz2 = N + ((double)v1[0] + (double)lg2(v2[0]));
+        break;
+      }
+      advance(t);
     }
     __syncthreads();  // phase-A history writes (incl. other lanes' N) visible to phase B
 
     // ---- phase B: backward messages rho, posterior and soft codeword, t = L-1 .. 0 -------
+    // Segment by segment (the whole chain is one segment with the full history); with
+    // checkpoints, each segment's forward offsets are replayed from its checkpoint first.
     MT rr[G][K];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int r = 0; r < K; ++r) rr[g][r] = (MT)0;
     double Np = 0.0;
-    MT lcn[G][K];
-    load_vec<KG>(hs + ((size_t)(L - 1) * BLOCK + tid) * KG, &lcn[0][0]);
-    double Nn = ns[(L - 1) * SPB + q];
-    for (long long t = L - 1; t >= 0; --t) {
-      MT lcur[G][K];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int a = 0; a < K; ++a) lcur[g][a] = lcn[g][a];
-      const double Nt = Nn;
-      if (t > 0) {
-        load_vec<KG>(hs + ((size_t)(t - 1) * BLOCK + tid) * KG, &lcn[0][0]);
-        Nn = ns[(t - 1) * SPB + q];
-      }
-      const float u = k.sc * wb[t];
-      const MT LZ = (MT)((lz2 - Nt) - Np);
-      float num = 0.f, den = 0.f;
-      MT mx = (MT)-INFINITY;
-      MT rout[G][K];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float Vg[K][K];
-        vsrc.get(g, Vg);
-#pragma unroll
-        for (int a = 0; a < K; ++a) {
-          MT y[K];
-          MT m = (MT)-INFINITY;
-#pragma unroll
-          for (int r = 0; r < K; ++r) {
-            y[r] = emit<P>(u, Vg[r][a], rr[g][r], k.kap);
-            m = tmax(m, y[r]);
-          }
-          float e0 = ex2((float)(y[0] - m));
-          float cs = e0, cw = Vg[0][a] * e0;
-#pragma unroll
-          for (int r = 1; r < K; ++r) {
-            const float e = ex2((float)(y[r] - m));
-            cs += e;
-            cw = __builtin_fmaf(Vg[r][a], e, cw);
-          }
-          rout[g][a] = m + (MT)lg2(cs);
-          mx = tmax(mx, rout[g][a]);
-          const float f = ex2((float)((m + lcur[g][a]) - LZ));
-          num = __builtin_fmaf(f, cw, num);
-          den = __builtin_fmaf(f, cs, den);
+    const long long nseg = seg ? ncp : 1;
+    for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
+      const long long t0 = seg ? sgi * seg : 0;
+      const long long t1 = seg ? (t0 + seg < L ? t0 + seg : L) : L;
+      if (CK) {
+        load_vec<KG>(hist(sgi), &lc[0][0]);
+        for (long long t = t0; t < t1; ++t) {
+          store_vec<KG>(hist(ncp + (t - t0)), &lc[0][0]);
+          if (t + 1 < t1) advance(t);
         }
       }
-      MT* mw = msg[mb] + q * M;
-      if (t > 0) {
+      auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
+      MT lcn[G][K];
+      load_vec<KG>(hist(entry(t1 - 1)), &lcn[0][0]);
+      double Nn = ns[(t1 - 1) * SPB + q];
+      for (long long t = t1 - 1; t >= t0; --t) {
+        MT lcur[G][K];
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int a = 0; a < K; ++a) mw[p + g * LPS + a * NG] = rout[g][a];
-      }
-      MT v3[3] = {(MT)num, (MT)den, mx};
-      chain_reduce<C, 3, 4u>(v3, red, rp);
-      if (valid && p == 0) {
-        const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
-        w_hat[b * L + t] = wh;
-        saved_what[b * L + t] = wh;
-      }
-      if (t == 0) break;
-      const MT sh = floor(v3[2]);
+          for (int a = 0; a < K; ++a) lcur[g][a] = lcn[g][a];
+        const double Nt = Nn;
+        if (t > t0) {
+          load_vec<KG>(hist(entry(t - 1)), &lcn[0][0]);
+          Nn = ns[(t - 1) * SPB + q];
+        }
+        const float u = k.sc * wb[t];
+        const MT LZ = (MT)((lz2 - Nt) - Np);
+        float num = 0.f, den = 0.f;
+        MT mx = (MT)-INFINITY;
+        MT rout[G][K];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        MT tmp[K];
-        load_vec<K>(mw + K * (p + g * LPS), tmp);
+        for (int g = 0; g < G; ++g) {
+          float Vg[K][K];
+          vsrc.get(g, Vg);
 #pragma unroll
-        for (int r = 0; r < K; ++r) rr[g][r] = tmp[r] - sh;
+          for (int a = 0; a < K; ++a) {
+            MT y[K];
+            MT m = (MT)-INFINITY;
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              y[r] = emit<P>(u, Vg[r][a], rr[g][r], k.kap);
+              m = tmax(m, y[r]);
+            }
+            float e0 = ex2((float)(y[0] - m));
+            float cs = e0, cw = Vg[0][a] * e0;
+#pragma unroll
+            for (int r = 1; r < K; ++r) {
+              const float e = ex2((float)(y[r] - m));
+              cs += e;
+              cw = __builtin_fmaf(Vg[r][a], e, cw);
+            }
+            rout[g][a] = m + (MT)lg2(cs);
+            mx = tmax(mx, rout[g][a]);
+            const float f = ex2((float)((m + lcur[g][a]) - LZ));
+            num = __builtin_fmaf(f, cw, num);
+            den = __builtin_fmaf(f, cs, den);
+          }
+        }
+        MT* mw = msg[mb] + q * M;
+        if (t > 0) {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int a = 0; a < K; ++a) mw[p + g * LPS + a * NG] = rout[g][a];
+        }
+        MT v3[3] = {(MT)num, (MT)den, mx};
+        chain_reduce<C, 3, 4u>(v3, red, rp);
+        if (valid && p == 0) {
+          const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
+          w_hat[b * L + t] = wh;
+          saved_what[b * L + t] = wh;
+        }
+        if (t == 0) break;
+        const MT sh = floor(v3[2]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          MT tmp[K];
+          load_vec<K>(mw + K * (p + g * LPS), tmp);
+#pragma unroll
+          for (int r = 0; r < K; ++r) rr[g][r] = tmp[r] - sh;
+        }
+        Np += (double)sh;
+        if constexpr (C::DB) mb ^= 1; else __syncthreads();
       }
-      Np += (double)sh;
-      if constexpr (C::DB) mb ^= 1; else __syncthreads();
     }
     if (valid && p == 0) {
       log_z[b] = (float)(lz2 * (double)kLn2);
@@ -451,17 +507,18 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 //   dF/dw_t  = (2/T) (sum_s c(s) E_t(s) - h w_t)
 //   dF/dc(s) = sum_t [ g_t gamma_t(s) + (2/T)(w_t - c(s)) E_t(s) ].
 // ---------------------------------------------------------------------------------------------
-template <class C>
+template <class C, bool CK>
 __global__ void __launch_bounds__(C::BLOCK)
 k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long long B, long long L,
              Consts k, const double* __restrict__ saved_lz, const float* __restrict__ saved_what,
              const float* __restrict__ gup, const float* __restrict__ hup,
              float* __restrict__ grad_w, float* __restrict__ partial, void* __restrict__ ws,
-             size_t slot_bytes, long long units) {
+             size_t slot_bytes, long long units, long long seg_arg) {
   using P = typename C::P;
   using MT = typename C::MT;
   constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
   constexpr int SPB = C::SPB, BLOCK = C::BLOCK;
+  const long long seg = CK ? seg_arg : 0;
   __shared__ __attribute__((aligned(16))) MT msgl[C::NBUF][SPB * M];
   __shared__ __attribute__((aligned(16))) float msgp[C::NBUF][SPB * M];
   __shared__ double red[2 * C::NWAVES * 4];
@@ -481,12 +538,16 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
       for (int a = 0; a < K; ++a) acc[g][r][a] = 0.f;
 
-  // slot layout: lam history [L][BLOCK][KG] (8-byte entries), Phi history [L][BLOCK][KG]
-  // (fp32), shift prefix N [L][SPB] (double)
+  // slot layout: lam history [H][BLOCK][KG] (8-byte entries), Phi history [H][BLOCK][KG]
+  // (fp32), shift prefix N [L][SPB] (double); H and the entry order as in k_sparse_fwd.
+  const long long ncp = seg ? (L + seg - 1) / seg : L;
+  const long long nh = seg ? ncp + seg : L;
   char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
   MT* __restrict__ hl = reinterpret_cast<MT*>(sb);
-  float* __restrict__ hp = reinterpret_cast<float*>(sb + (size_t)L * BLOCK * KG * 8);
-  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)L * BLOCK * KG * 12);
+  float* __restrict__ hp = reinterpret_cast<float*>(sb + (size_t)nh * BLOCK * KG * 8);
+  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * BLOCK * KG * 12);
+  auto histl = [&](long long e) { return hl + ((size_t)e * BLOCK + tid) * KG; };
+  auto histp = [&](long long e) { return hp + ((size_t)e * BLOCK + tid) * KG; };
   int mb = 0, rp = 0;
 
   for (long long unit = blockIdx.x; unit < units; unit += gridDim.x) {
@@ -499,7 +560,6 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
     const float h = (hup != nullptr && valid) ? hup[bb] : 0.f;
     const double lz2 = saved_lz[bb];
 
-    // ---- phase A: lam and Phi, t = 0 .. L-1 ----------------------------------------------
     MT lc[G][K];
     float pc[G][K];
 #pragma unroll
@@ -507,11 +567,9 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
       for (int a = 0; a < K; ++a) { lc[g][a] = (MT)0; pc[g][a] = 0.f; }
     double N = 0.0;
-    for (long long t = 0; t < L; ++t) {
-      store_vec<KG>(hl + ((size_t)t * BLOCK + tid) * KG, &lc[0][0]);
-      store_vec<KG>(hp + ((size_t)t * BLOCK + tid) * KG, &pc[0][0]);
-      if (p == 0) ns[t * SPB + q] = N;
-      if (t == L - 1) break;
+
+    // One forward step: (lam, Phi) column offsets of step t -> those of step t + 1 (t < L - 1).
+    auto advance = [&](long long t) {
       const float u = k.sc * wb[t];
       const float gtp = gb[t] * k.csc;     // g_t c(s) = gtp * v(s)
       const float gwh = gb[t] * whb[t];    // g_t w_hat_t
@@ -568,10 +626,24 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         }
       N += (double)sh;
       if constexpr (C::DB) mb ^= 1; else __syncthreads();
+    };
+
+    // ---- phase A: lam and Phi, t = 0 .. L-1 ----------------------------------------------
+    for (long long t = 0; t < L; ++t) {
+      if (seg == 0 || t % seg == 0) {
+        const long long e = seg ? t / seg : t;
+        store_vec<KG>(histl(e), &lc[0][0]);
+        store_vec<KG>(histp(e), &pc[0][0]);
+      }
+      if (p == 0) ns[t * SPB + q] = N;
+      if (t == L - 1) break;
+      advance(t);
     }
     __syncthreads();
 
     // ---- phase B: rho and Psi, posterior, D, gradients, t = L-1 .. 0 ---------------------
+    // Segment by segment, replaying each segment's forward offsets from its checkpoint first
+    // when the history is checkpointed (one segment of length L otherwise).
     MT rr[G][K];
     float qr[G][K];
 #pragma unroll
@@ -579,109 +651,124 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
       for (int r = 0; r < K; ++r) { rr[g][r] = (MT)0; qr[g][r] = 0.f; }
     double Np = 0.0;
-    MT lcn[G][K];
-    float pcn[G][K];
-    load_vec<KG>(hl + ((size_t)(L - 1) * BLOCK + tid) * KG, &lcn[0][0]);
-    load_vec<KG>(hp + ((size_t)(L - 1) * BLOCK + tid) * KG, &pcn[0][0]);
-    double Nn = ns[(L - 1) * SPB + q];
-    for (long long t = L - 1; t >= 0; --t) {
-      MT lcur[G][K];
-      float pcur[G][K];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int a = 0; a < K; ++a) { lcur[g][a] = lcn[g][a]; pcur[g][a] = pcn[g][a]; }
-      const double Nt = Nn;
-      if (t > 0) {
-        load_vec<KG>(hl + ((size_t)(t - 1) * BLOCK + tid) * KG, &lcn[0][0]);
-        load_vec<KG>(hp + ((size_t)(t - 1) * BLOCK + tid) * KG, &pcn[0][0]);
-        Nn = ns[(t - 1) * SPB + q];
-      }
-      const float u = k.sc * wb[t];
-      const float gt = gb[t];
-      const float gtp = gt * k.csc;
-      const float gwh = gt * whb[t];
-      const MT LZ = (MT)((lz2 - Nt) - Np);
-      float qrc[G][K];  // Psi_t - g_t w_hat_t at the row offsets
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int r = 0; r < K; ++r) qrc[g][r] = qr[g][r] - gwh;
-      float gw = 0.f;
-      MT mx = (MT)-INFINITY;
-      MT rout[G][K];
-      float qout[G][K];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float Vg[K][K];
-        vsrc.get(g, Vg);
-#pragma unroll
-        for (int a = 0; a < K; ++a) {
-          MT y[K];
-          float dd[K];
-          MT m = (MT)-INFINITY;
-#pragma unroll
-          for (int r = 0; r < K; ++r) {
-            dd[r] = u - Vg[r][a];
-            y[r] = emit<P>(u, Vg[r][a], rr[g][r], k.kap);
-            m = tmax(m, y[r]);
-          }
-          float e[K], t2[K];
-#pragma unroll
-          for (int r = 0; r < K; ++r) {
-            e[r] = ex2((float)(y[r] - m));
-            t2[r] = __builtin_fmaf(gtp, Vg[r][a], qrc[g][r]);
-          }
-          float cs = e[0], ps = e[0] * t2[0];
-#pragma unroll
-          for (int r = 1; r < K; ++r) {
-            cs += e[r];
-            ps = __builtin_fmaf(e[r], t2[r], ps);
-          }
-          rout[g][a] = m + (MT)lg2(cs);
-          qout[g][a] = ps * rcp_nr(cs);
-          mx = tmax(mx, rout[g][a]);
-          const float f = ex2((float)((m + lcur[g][a]) - LZ));
-          const float pa = pcur[g][a] + h;
-          if (valid) {
-#pragma unroll
-            for (int r = 0; r < K; ++r) {
-              const float gm = e[r] * f;
-              const float eh = gm * (t2[r] + pa);
-              gw = __builtin_fmaf(Vg[r][a], eh, gw);
-              acc[g][r][a] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, acc[g][r][a]));
-            }
-          }
+    const long long nseg = seg ? ncp : 1;
+    for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
+      const long long t0 = seg ? sgi * seg : 0;
+      const long long t1 = seg ? (t0 + seg < L ? t0 + seg : L) : L;
+      if (CK) {
+        load_vec<KG>(histl(sgi), &lc[0][0]);
+        load_vec<KG>(histp(sgi), &pc[0][0]);
+        for (long long t = t0; t < t1; ++t) {
+          store_vec<KG>(histl(ncp + (t - t0)), &lc[0][0]);
+          store_vec<KG>(histp(ncp + (t - t0)), &pc[0][0]);
+          if (t + 1 < t1) advance(t);
         }
       }
-      MT* mw = msgl[mb] + q * M;
-      float* pw = msgp[mb] + q * M;
-      if (t > 0) {
+      auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
+      MT lcn[G][K];
+      float pcn[G][K];
+      load_vec<KG>(histl(entry(t1 - 1)), &lcn[0][0]);
+      load_vec<KG>(histp(entry(t1 - 1)), &pcn[0][0]);
+      double Nn = ns[(t1 - 1) * SPB + q];
+      for (long long t = t1 - 1; t >= t0; --t) {
+        MT lcur[G][K];
+        float pcur[G][K];
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
+          for (int a = 0; a < K; ++a) { lcur[g][a] = lcn[g][a]; pcur[g][a] = pcn[g][a]; }
+        const double Nt = Nn;
+        if (t > t0) {
+          load_vec<KG>(histl(entry(t - 1)), &lcn[0][0]);
+          load_vec<KG>(histp(entry(t - 1)), &pcn[0][0]);
+          Nn = ns[(t - 1) * SPB + q];
+        }
+        const float u = k.sc * wb[t];
+        const float gt = gb[t];
+        const float gtp = gt * k.csc;
+        const float gwh = gt * whb[t];
+        const MT LZ = (MT)((lz2 - Nt) - Np);
+        float qrc[G][K];  // Psi_t - g_t w_hat_t at the row offsets
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < K; ++r) qrc[g][r] = qr[g][r] - gwh;
+        float gw = 0.f;
+        MT mx = (MT)-INFINITY;
+        MT rout[G][K];
+        float qout[G][K];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float Vg[K][K];
+          vsrc.get(g, Vg);
+#pragma unroll
           for (int a = 0; a < K; ++a) {
-            mw[p + g * LPS + a * NG] = rout[g][a];
-            pw[p + g * LPS + a * NG] = qout[g][a];
+            MT y[K];
+            float dd[K];
+            MT m = (MT)-INFINITY;
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              dd[r] = u - Vg[r][a];
+              y[r] = emit<P>(u, Vg[r][a], rr[g][r], k.kap);
+              m = tmax(m, y[r]);
+            }
+            float e[K], t2[K];
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              e[r] = ex2((float)(y[r] - m));
+              t2[r] = __builtin_fmaf(gtp, Vg[r][a], qrc[g][r]);
+            }
+            float cs = e[0], ps = e[0] * t2[0];
+#pragma unroll
+            for (int r = 1; r < K; ++r) {
+              cs += e[r];
+              ps = __builtin_fmaf(e[r], t2[r], ps);
+            }
+            rout[g][a] = m + (MT)lg2(cs);
+            qout[g][a] = ps * rcp_nr(cs);
+            mx = tmax(mx, rout[g][a]);
+            const float f = ex2((float)((m + lcur[g][a]) - LZ));
+            const float pa = pcur[g][a] + h;
+            if (valid) {
+#pragma unroll
+              for (int r = 0; r < K; ++r) {
+                const float gm = e[r] * f;
+                const float eh = gm * (t2[r] + pa);
+                gw = __builtin_fmaf(Vg[r][a], eh, gw);
+                acc[g][r][a] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, acc[g][r][a]));
+              }
+            }
           }
-      }
-      MT v2[2] = {(MT)gw, mx};
-      chain_reduce<C, 2, 2u>(v2, red, rp);
-      if (valid && p == 0)
-        grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
-      if (t == 0) break;
-      const MT sh = floor(v2[1]);
+        }
+        MT* mw = msgl[mb] + q * M;
+        float* pw = msgp[mb] + q * M;
+        if (t > 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        MT tm[K];
-        float tp[K];
-        load_vec<K>(mw + K * (p + g * LPS), tm);
-        load_vec<K>(pw + K * (p + g * LPS), tp);
+          for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int r = 0; r < K; ++r) { rr[g][r] = tm[r] - sh; qr[g][r] = tp[r]; }
+            for (int a = 0; a < K; ++a) {
+              mw[p + g * LPS + a * NG] = rout[g][a];
+              pw[p + g * LPS + a * NG] = qout[g][a];
+            }
+        }
+        MT v2[2] = {(MT)gw, mx};
+        chain_reduce<C, 2, 2u>(v2, red, rp);
+        if (valid && p == 0)
+          grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+        if (t == 0) break;
+        const MT sh = floor(v2[1]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          MT tm[K];
+          float tp[K];
+          load_vec<K>(mw + K * (p + g * LPS), tm);
+          load_vec<K>(pw + K * (p + g * LPS), tp);
+#pragma unroll
+          for (int r = 0; r < K; ++r) { rr[g][r] = tm[r] - sh; qr[g][r] = tp[r]; }
+        }
+        Np += (double)sh;
+        if constexpr (C::DB) mb ^= 1; else __syncthreads();
       }
-      Np += (double)sh;
-      if constexpr (C::DB) mb ^= 1; else __syncthreads();
     }
   }
 
@@ -742,35 +829,52 @@ Consts make_consts(float T, bool precise) {
 
 template <int n, int k, class P>
 int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
-              float T, float* w_hat, float* log_z, float* saved, void* ws, hipStream_t st) {
+              float T, float* w_hat, float* log_z, float* saved, void* ws, bool ckpt,
+              hipStream_t st) {
   using C = Cfg<(1 << k), geom_g(n, k, kFwd), geom_lps(n, k, kFwd), P, false>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   const Consts kc = make_consts(T, P::kPrecise);
-  const size_t slot = sparse_fwd_slot_bytes(g, L);
+  const size_t slot = sparse_fwd_slot_bytes(g, L, ckpt);
+  const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
   double* slz = reinterpret_cast<double*>(saved);
   float* swh = saved + saved_what_offset(B);
-  const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_fwd<C>), C::BLOCK, g.slots);
+  const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_fwd<C, true>)
+                          : reinterpret_cast<const void*>(&k_sparse_fwd<C, false>);
+  const int grid = resident_grid(kern, C::BLOCK, g.slots);
   if (grid <= 0) return (int)hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_sparse_fwd<C>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w, B, L,
-                     kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units);
+  if (ckpt)
+    hipLaunchKernelGGL((k_sparse_fwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
+                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg);
+  else
+    hipLaunchKernelGGL((k_sparse_fwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
+                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg);
   return (int)hipGetLastError();
 }
 
 template <int n, int k, class P>
 int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, const float* saved, const float* gup, const float* hup, float* grad_w,
-              float* grad_c, void* ws, hipStream_t st) {
+              float* grad_c, void* ws, bool ckpt, hipStream_t st) {
   using C = Cfg<(1 << k), geom_g(n, k, kBwd), geom_lps(n, k, kBwd), P, true>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   const Consts kc = make_consts(T, P::kPrecise);
-  const size_t slot = sparse_bwd_slot_bytes(g, L);
+  const size_t slot = sparse_bwd_slot_bytes(g, L, ckpt);
+  const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + slot * (size_t)g.slots);
   const double* slz = reinterpret_cast<const double*>(saved);
   const float* swh = saved + saved_what_offset(B);
-  const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_bwd<C>), C::BLOCK, g.slots);
+  const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_bwd<C, true>)
+                          : reinterpret_cast<const void*>(&k_sparse_bwd<C, false>);
+  const int grid = resident_grid(kern, C::BLOCK, g.slots);
   if (grid <= 0) return (int)hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_sparse_bwd<C>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w, B, L,
-                     kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units);
+  if (ckpt)
+    hipLaunchKernelGGL((k_sparse_bwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
+                       B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units,
+                       seg);
+  else
+    hipLaunchKernelGGL((k_sparse_bwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
+                       B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units,
+                       seg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((C::S + 255) / 256)), dim3(256), 0, st, partial,
@@ -780,21 +884,23 @@ int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
 
 template <int n, int k>
 int run_fwd(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
-            float T, float* w_hat, float* log_z, float* saved, void* ws, hipStream_t st) {
+            float T, float* w_hat, float* log_z, float* saved, void* ws, bool ckpt,
+            hipStream_t st) {
   if constexpr (precise_fits<n, k>())
     if (use_precise<n, k>(T))
-      return run_fwd_p<n, k, Precise>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, st);
-  return run_fwd_p<n, k, Fast>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, st);
+      return run_fwd_p<n, k, Precise>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+  return run_fwd_p<n, k, Fast>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
 }
 
 template <int n, int k>
 int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
             float T, const float* saved, const float* gup, const float* hup, float* grad_w,
-            float* grad_c, void* ws, hipStream_t st) {
+            float* grad_c, void* ws, bool ckpt, hipStream_t st) {
   if constexpr (precise_fits<n, k>())
     if (use_precise<n, k>(T))
-      return run_bwd_p<n, k, Precise>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, st);
-  return run_bwd_p<n, k, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, st);
+      return run_bwd_p<n, k, Precise>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt,
+                                      st);
+  return run_bwd_p<n, k, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt, st);
 }
 
 }  // namespace
@@ -806,10 +912,11 @@ int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
 
 int launch_sparse_forward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                           int64_t L, float T, float* w_hat, float* log_z, float* saved, void* ws,
-                          void* stream) {
+                          bool ckpt, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-#define X(N_, K_) \
-  if (g.n == N_ && g.k == K_) return run_fwd<N_, K_>(g, codebook, w, B, L, T, w_hat, log_z, saved, ws, st);
+#define X(N_, K_)                                                                              \
+  if (g.n == N_ && g.k == K_)                                                                  \
+    return run_fwd<N_, K_>(g, codebook, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
   BCJR_SPARSE_SHAPES(X)
 #undef X
   return (int)hipErrorInvalidValue;
@@ -818,12 +925,12 @@ int launch_sparse_forward(const SparseGeom& g, const float* codebook, const floa
 int launch_sparse_backward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                            int64_t L, float T, const float* saved, const float* grad_w_hat,
                            const float* grad_log_z, float* grad_w, float* grad_codebook, void* ws,
-                           void* stream) {
+                           bool ckpt, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
 #define X(N_, K_)                                                                          \
   if (g.n == N_ && g.k == K_)                                                              \
     return run_bwd<N_, K_>(g, codebook, w, B, L, T, saved, grad_w_hat, grad_log_z, grad_w, \
-                           grad_codebook, ws, st);
+                           grad_codebook, ws, ckpt, st);
   BCJR_SPARSE_SHAPES(X)
 #undef X
   return (int)hipErrorInvalidValue;

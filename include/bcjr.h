@@ -72,10 +72,16 @@ int bcjr_supported(const bcjr_trellis* tr);
  * for an invalid shape. Host only, needs no device. */
 size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L);
 
-/* Bytes of device workspace for a call: which = 0 forward, 1 backward, 2 viterbi.
+/* Bytes of device workspace for a call: which = 0 forward, 1 backward, 2 viterbi, 3 forward
+ * with checkpointed history, 4 backward with checkpointed history.
  * Returns 0 for an invalid shape or flag. Host only, needs no device. The workspace holds
  * per-slot message histories (the alpha-side messages of one sweep, read back by the
- * sweep in the other direction) and, for the backward, per-slot codebook-gradient partials. */
+ * sweep in the other direction; a slot is one chain, or a few narrow chains, in flight) and,
+ * for the backward, per-slot codebook-gradient partials. The full history keeps every step (L
+ * entries per slot); the checkpointed one keeps every C-th step, C = ceil(sqrt(L)), and the
+ * reverse sweep recomputes one segment of C steps at a time (about 2 sqrt(L) entries per slot,
+ * for one more forward recursion of work; results are bitwise identical). bcjr_forward and
+ * bcjr_backward use the full history when ws_bytes covers it, else the checkpointed one. */
 size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int which);
 
 /*
@@ -88,7 +94,8 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
  * w_hat  DEVICE [B,L]  written
  * log_z  DEVICE [B]    written
  * saved  DEVICE, bcjr_saved_bytes() bytes, written; pass it unchanged to bcjr_backward
- * ws     DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 0); contents are scratch
+ * ws     DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 3) (checkpointed history) or
+ *        >= bcjr_workspace_bytes(tr, B, L, 0) (full history); contents are scratch
  * B = 0 is valid and enqueues nothing.
  */
 bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
@@ -105,7 +112,8 @@ bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int6
  * grad_log_z DEVICE [B] upstream gradient h, or NULL for h = 0
  * grad_w     DEVICE [B,L] written
  * grad_codebook DEVICE [S] written (overwritten, summed over all B chains, fixed-order sum)
- * ws         DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 1)
+ * ws         DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 4) (checkpointed history) or
+ *            >= bcjr_workspace_bytes(tr, B, L, 1) (full history)
  */
 bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                           const void* saved, const float* grad_w_hat, const float* grad_log_z,

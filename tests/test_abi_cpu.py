@@ -92,8 +92,9 @@ def test_forward_rejects_bad_arguments_without_device(lib):
     assert _fwd(lib, wh=0) == bcjr.BCJR_E_ARG
     assert _fwd(lib, sv=0) == bcjr.BCJR_E_ARG
     assert _fwd(lib, ws=0) == bcjr.BCJR_E_WORKSPACE
-    need = bcjr.bcjr_workspace_bytes(8, 2, 4, 8, bcjr.FWD)
+    need = bcjr.bcjr_workspace_bytes(8, 2, 4, 8, bcjr.FWD_CKPT)  # the smaller, checkpointed layout
     assert _fwd(lib, wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
+    assert _fwd(lib, ws=0x6008) == bcjr.BCJR_E_WORKSPACE  # 16-byte alignment
     # B = 0 is valid and enqueues nothing (null outputs allowed)
     assert _fwd(lib, B=0, w=0, wh=0, lz=0, sv=0, ws=0, wsb=0) == bcjr.BCJR_OK
 
@@ -113,6 +114,7 @@ def test_backward_and_viterbi_reject_bad_arguments_without_device(lib):
     assert bwd(sv=P(0)) == bcjr.BCJR_E_ARG
     assert bwd(g=P(0)) == bcjr.BCJR_E_ARG
     assert bwd(wsb=0) == bcjr.BCJR_E_WORKSPACE
+    assert bwd(wsb=bcjr.bcjr_workspace_bytes(8, 2, 4, 8, bcjr.BWD_CKPT) - 1) == bcjr.BCJR_E_WORKSPACE
     assert bwd(L=0) == bcjr.BCJR_E_SHAPE
 
     def vit(B=4, L=8, wsb=1 << 40, st=P(0x8000), ws=P(0x7000)):
@@ -192,3 +194,18 @@ def test_autograd_wrapper_refuses_cpu_tensors():
         autograd.soft_quantize(w, c, 4, 2, 0.5)
     with pytest.raises(ValueError):
         autograd.dense_soft_quantize(w, torch.zeros(32), torch.zeros((32, 32)), 0.5)
+
+
+def test_checkpointed_workspace_sizes(lib):
+    # checkpoints every C = ceil(sqrt(L)) steps plus one C-step replay buffer per slot
+    for n, L in [(12, 256), (16, 256), (8, 1000), (16, 4096)]:
+        for full, ck in [(bcjr.FWD, bcjr.FWD_CKPT), (bcjr.BWD, bcjr.BWD_CKPT)]:
+            f = bcjr.bcjr_workspace_bytes(n, 2, 4096, L, full)
+            c = bcjr.bcjr_workspace_bytes(n, 2, 4096, L, ck)
+            assert 0 < c < f
+    # at S = 65536, L = 4096 the full forward history is 128x the checkpointed one's history
+    f = bcjr.bcjr_workspace_bytes(16, 2, 16384, 4096, bcjr.FWD)
+    c = bcjr.bcjr_workspace_bytes(16, 2, 16384, 4096, bcjr.FWD_CKPT)
+    assert f > 200 * 2**30 and c < 16 * 2**30
+    assert bcjr.bcjr_workspace_bytes(8, 2, 16, 16, 5) == 0
+    assert bcjr.bcjr_workspace_bytes(8, 2, 0, 16, bcjr.BWD_CKPT) == 0

@@ -1,0 +1,93 @@
+"""Checkpointed message histories: the same results as the full history, from about 2 sqrt(L)
+history entries per slot instead of L (the reverse sweep replays each segment of C = ceil(sqrt(L))
+steps from its checkpoint)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bcjr_soft_decoding_amd import bcjr, synth
+from tests.gpu_helpers import RTOL_FWD, RTOL_GRAD, assert_normwise, assert_rel, dev, log_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bcjr.lib()
+
+
+def _run(n, k, c, w, g, h, T, ckpt):
+    B, L = w.shape
+    cd, wd = dev(c), dev(w)
+    wf = bcjr.workspace(n, k, B, L, bcjr.FWD_CKPT if ckpt else bcjr.FWD)
+    wb = bcjr.workspace(n, k, B, L, bcjr.BWD_CKPT if ckpt else bcjr.BWD)
+    w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, k, T, ws=wf)
+    gw, gc = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), None if h is None else dev(h), ws=wb)
+    torch.cuda.synchronize()
+    return {"w_hat": w_hat.cpu().numpy(), "log_z": log_z.cpu().numpy(), "grad_w": gw.cpu().numpy(),
+            "grad_codebook": gc.cpu().numpy()}
+
+
+CASES = [
+    (8, 9, 256, 0.3),    # L a perfect square (C = 16)
+    (8, 5, 37, 0.3),     # ragged last segment
+    (12, 3, 100, 0.1),   # workload-3 geometry
+    (4, 65, 17, 1.0),    # several chains per wave
+    (6, 2, 1, 0.5),      # L = 1
+    (6, 3, 2, 0.5),
+    (16, 2, 20, 0.3),    # 16-wave chains
+    (8, 4, 64, 0.01),    # fp64 messages
+]
+
+
+@pytest.mark.parametrize("n,B,L,T", CASES)
+def test_checkpointed_equals_full_history(n, B, L, T):
+    k = 2
+    c = synth.normal(9000 + n, (1 << n,))
+    w = synth.normal(9100 + n + L, (B, L))
+    g = synth.normal(9200 + n + L, (B, L))
+    h = synth.normal(9300 + n, (B,))
+    log_case(f"checkpoint vs full n={n} B={B} L={L} T={T}")
+    full = _run(n, k, c, w, g, h, T, False)
+    ck = _run(n, k, c, w, g, h, T, True)
+    # per-chain results replay the same arithmetic: bitwise equal
+    for key in ("w_hat", "log_z", "grad_w"):
+        np.testing.assert_array_equal(ck[key], full[key], err_msg=key)
+    # the codebook gradient sums slot partials; the two kernels may run different grids
+    assert_normwise(ck["grad_codebook"], full["grad_codebook"], 1e-6, "grad_c")
+
+
+def test_checkpointed_matches_oracle():
+    n, k, T = 10, 2, 0.2
+    c = synth.normal(9400, (1 << n,))
+    w = synth.normal(9401, (6, 129))
+    g = synth.normal(9402, (6, 129))
+    log_case("checkpointed vs oracle n=10 B=6 L=129")
+    got = _run(n, k, c, w, g, None, T, True)
+    rf = oracle.sparse_forward(n, k, c, w, T)
+    rb = oracle.sparse_backward(n, k, c, w, T, g)
+    assert_normwise(got["w_hat"], rf["w_hat"], RTOL_FWD, "w_hat")
+    assert_rel(got["log_z"], rf["log_z"], RTOL_FWD, "log_z")
+    assert_normwise(got["grad_w"], rb["grad_w"], RTOL_GRAD, "grad_w")
+    assert_normwise(got["grad_codebook"], rb["grad_codebook"], RTOL_GRAD, "grad_c")
+
+
+def test_long_chains_at_2_16_states_fit_with_checkpoints():
+    """S = 65536, L = 4096: the checkpointed workspace is used (the full history would be
+    128x larger per slot); sampled against the full-history run on the same chains."""
+    n, k, T = 16, 2, 0.3
+    B, L = 2, 4096
+    c = synth.normal(9500, (1 << n,))
+    w = synth.normal(9501, (B, L))
+    g = synth.normal(9502, (B, L))
+    log_case("S=65536 L=4096 checkpointed")
+    full_b = bcjr.bcjr_workspace_bytes(n, k, B, L, bcjr.BWD)
+    ck_b = bcjr.bcjr_workspace_bytes(n, k, B, L, bcjr.BWD_CKPT)
+    assert ck_b * 20 < full_b
+    ck = _run(n, k, c, w, g, None, T, True)
+    full = _run(n, k, c, w, g, None, T, False)
+    for key in ("w_hat", "log_z", "grad_w"):
+        np.testing.assert_array_equal(ck[key], full[key], err_msg=key)
+    assert np.all(np.isfinite(ck["grad_codebook"]))
