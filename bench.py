@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--temp", type=float, default=None)
+    ap.add_argument("--history", choices=["full", "ckpt"], default="full",
+                    help="bitshift message histories: every step, or checkpoints + segment replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1536, help="chains timed on the CPU oracle")
     ap.add_argument("--cpu-sample-dense", type=int, default=64,
@@ -275,8 +277,9 @@ def main():
     saved = torch.empty(bcjr.bcjr_saved_bytes(n, k, B, L), dtype=torch.uint8, device=dev)
     grad_w = torch.empty_like(w)
     grad_c = torch.empty_like(c)
-    wsf = bcjr.workspace(n, k, B, L, bcjr.FWD, dev)
-    wsb = bcjr.workspace(n, k, B, L, bcjr.BWD, dev)
+    ck = args.history == "ckpt"
+    wsf = bcjr.workspace(n, k, B, L, bcjr.FWD_CKPT if ck else bcjr.FWD, dev)
+    wsb = bcjr.workspace(n, k, B, L, bcjr.BWD_CKPT if ck else bcjr.BWD, dev)
 
     def step(ev=None):
         if ev is not None:
@@ -321,6 +324,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "L": L, "S": S, "k": k, "T": T,
+                   "history": args.history, "workspace_bytes": int(wsf.numel() + wsb.numel()),
                    "parallelism": "single-gpu"},
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
         "roofline": {
