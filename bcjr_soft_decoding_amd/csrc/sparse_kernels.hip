@@ -134,6 +134,34 @@ __device__ __forceinline__ double dpp(double v) {
 template <class T>
 __device__ __forceinline__ T comb(T a, T b, bool is_max) { return is_max ? tmax(a, b) : a + b; }
 
+// comb of v with the value of lane l ^ 16 (X32 false) or l ^ 32 (X32 true): a register swapped
+// with itself by v_permlane16_swap / v_permlane32_swap holds {own, partner} in its two results
+// (in either order), and comb is commutative, so every lane of a pair gets the same bits.
+// A VALU move, no LDS round trip.
+template <bool X32>
+__device__ __forceinline__ void swap_self(unsigned u, unsigned& r0, unsigned& r1) {
+  const auto r = X32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                     : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  r0 = r[0];
+  r1 = r[1];
+}
+template <bool X32>
+__device__ __forceinline__ float xor_comb(float v, bool is_max) {
+  unsigned r0, r1;
+  swap_self<X32>(__float_as_uint(v), r0, r1);
+  return comb(__uint_as_float(r0), __uint_as_float(r1), is_max);
+}
+template <bool X32>
+__device__ __forceinline__ double xor_comb(double v, bool is_max) {
+  const long long b = __double_as_longlong(v);
+  unsigned l0, l1, h0, h1;
+  swap_self<X32>((unsigned)(b & 0xffffffffLL), l0, l1);
+  swap_self<X32>((unsigned)(b >> 32), h0, h1);
+  const double d0 = __longlong_as_double(((long long)h0 << 32) | l0);
+  const double d1 = __longlong_as_double(((long long)h1 << 32) | l1);
+  return comb(d0, d1, is_max);
+}
+
 // Reduction over aligned groups of W lanes inside a wave. Every step combines two disjoint
 // halves symmetrically (a op b in one half, b op a in the other), so every lane of the group
 // ends with the bitwise-identical result.
@@ -143,8 +171,8 @@ __device__ __forceinline__ T lanes_reduce(T v, bool is_max) {
   if constexpr (W >= 4) v = comb(v, dpp<0x4E>(v), is_max);
   if constexpr (W >= 8) v = comb(v, dpp<0x141>(v), is_max);
   if constexpr (W >= 16) v = comb(v, dpp<0x140>(v), is_max);
-  if constexpr (W >= 32) v = comb(v, __shfl_xor(v, 16, 64), is_max);
-  if constexpr (W >= 64) v = comb(v, __shfl_xor(v, 32, 64), is_max);
+  if constexpr (W >= 32) v = xor_comb<false>(v, is_max);
+  if constexpr (W >= 64) v = xor_comb<true>(v, is_max);
   return v;
 }
 
@@ -161,18 +189,19 @@ __device__ __forceinline__ void chain_reduce(T (&v)[NV], double* red, int& rp) {
   } else {
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = lanes_reduce<64>(v[i], (MASK >> i) & 1u);
-    double* r = red + rp * (C::NWAVES * 4);
+    // per-wave partials in their own type (the double buffer holds either)
+    T* r = reinterpret_cast<T*>(red) + rp * (C::NWAVES * 4);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) r[wave * 4 + i] = (double)v[i];
+      for (int i = 0; i < NV; ++i) r[wave * 4 + i] = v[i];
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      T acc = (T)r[i];
+      T acc = r[i];
       for (int wv = 1; wv < C::NWAVES; ++wv)
-        acc = ((MASK >> i) & 1u) ? tmax(acc, (T)r[wv * 4 + i]) : acc + (T)r[wv * 4 + i];
+        acc = ((MASK >> i) & 1u) ? tmax(acc, r[wv * 4 + i]) : acc + r[wv * 4 + i];
       v[i] = acc;
     }
     rp ^= 1;
@@ -729,6 +758,8 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             mx = tmax(mx, rout[g][a]);
             const float f = ex2((float)((m + lcur[g][a]) - LZ));
             const float pa = pcur[g][a] + h;
+            // (a uniform branch per 4x4 block: it also bounds the live ranges the scheduler
+            // builds across blocks, which keeps this kernel at two waves per SIMD)
             if (valid) {
 #pragma unroll
               for (int r = 0; r < K; ++r) {

@@ -48,7 +48,8 @@ PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # HBM traffic of the profiled kernel, read from the committed rocprofv3 summary; reported only
 # while the kernel sources still hash to the value recorded there.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_sparse_bwd_llama32-1b-mlp-up-s4096_pmc.md")
-KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_decoding_amd/csrc/geom.h"]
+KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_decoding_amd/csrc/geom.h",
+                  "bcjr_soft_decoding_amd/csrc/internal.h", "bcjr_soft_decoding_amd/build.py"]
 
 
 def op_slots(kernel: str) -> float:

@@ -30,7 +30,8 @@
  *     nothing is enqueued and no output buffer is touched.
  *   - Calls are asynchronous on the given stream (NULL = the default stream) and never
  *     synchronise. A launch failure is reported as BCJR_E_DEVICE by the call that sees it.
- *   - NaN or Inf in w, the codebook or theta propagate to the outputs unchecked.
+ *   - Inputs are not checked for NaN or Inf: the forward-backward entry points assume finite
+ *     w, codebook and theta (NaN gives unspecified outputs); the Viterbi decoder is IEEE-exact.
  *   - Results are bitwise deterministic for a given device, input and argument set.
  *   - The library is thread safe (no shared mutable state); use one stream per thread.
  */
