@@ -22,7 +22,7 @@ EXPORTED = (
     "bcjr_supported", "bcjr_saved_bytes", "bcjr_workspace_bytes", "bcjr_forward",
     "bcjr_backward", "viterbi_decode", "bcjr_dense_supported", "bcjr_dense_saved_bytes",
     "bcjr_dense_workspace_bytes", "bcjr_dense_forward", "bcjr_dense_backward",
-    "bcjr_status_string",
+    "bcjr_code_words", "bcjr_pack_code", "bcjr_unpack_code", "bcjr_status_string",
 )
 
 
@@ -77,6 +77,12 @@ def lib() -> ctypes.CDLL:
     L.bcjr_dense_forward.restype = ctypes.c_int
     L.bcjr_dense_backward.argtypes = [I32, P, P, P, I64, I64, F, P, P, P, P, P, P, P, SZ, P]
     L.bcjr_dense_backward.restype = ctypes.c_int
+    L.bcjr_code_words.argtypes = [TP, I64]
+    L.bcjr_code_words.restype = I64
+    L.bcjr_pack_code.argtypes = [TP, P, I64, I64, P, P]
+    L.bcjr_pack_code.restype = ctypes.c_int
+    L.bcjr_unpack_code.argtypes = [TP, P, I64, I64, P, P, P]
+    L.bcjr_unpack_code.restype = ctypes.c_int
     L.bcjr_status_string.argtypes = [ctypes.c_int]
     L.bcjr_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -246,3 +252,43 @@ def bcjr_dense_backward(theta, codebook, w, T, saved, grad_w_hat, grad_log_z=Non
                                    _stream())
     _check(st, "bcjr_dense_backward")
     return grad_w, grad_codebook, grad_theta
+
+
+# ---- hard-code export (bitshift trellis) --------------------------------------------------------
+
+def bcjr_code_words(n: int, k: int, L: int) -> int:
+    tr = trellis(n, k)
+    return int(lib().bcjr_code_words(ctypes.byref(tr), L))
+
+
+def bcjr_pack_code(states, n, k, code=None):
+    """Pack int32 state paths [B,L] into uint32 codes [B, words] (n bits of s_0, then k bits per
+    step, most significant first)."""
+    if not (states.dtype == torch.int32 and states.is_cuda and states.is_contiguous()):
+        raise ValueError("states must be a contiguous int32 CUDA tensor")
+    B, L = states.shape
+    if code is None:
+        code = torch.empty((B, max(bcjr_code_words(n, k, L), 1)), dtype=torch.uint32,
+                           device=states.device)
+    tr = trellis(n, k)
+    st = lib().bcjr_pack_code(ctypes.byref(tr), _ptr(states), B, L, _ptr(code), _stream())
+    _check(st, "bcjr_pack_code")
+    return code
+
+
+def bcjr_unpack_code(code, n, k, L, codebook=None, states=None, w_hard=None):
+    """States int32 [B,L] (and w_hard = c(states) if a codebook is given) from uint32 codes."""
+    if not (code.dtype == torch.uint32 and code.is_cuda and code.is_contiguous()):
+        raise ValueError("code must be a contiguous uint32 CUDA tensor")
+    B = code.shape[0]
+    dev = code.device
+    states = torch.empty((B, L), dtype=torch.int32, device=dev) if states is None else states
+    if codebook is not None:
+        _f32(codebook, "codebook")
+        if w_hard is None:
+            w_hard = torch.empty((B, L), dtype=torch.float32, device=dev)
+    tr = trellis(n, k, codebook)
+    st = lib().bcjr_unpack_code(ctypes.byref(tr), _ptr(code), B, L, _ptr(states), _ptr(w_hard),
+                                _stream())
+    _check(st, "bcjr_unpack_code")
+    return states, w_hard

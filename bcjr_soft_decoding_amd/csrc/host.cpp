@@ -189,6 +189,32 @@ bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, in
   return from_hip(launch_viterbi(g, tr->codebook, w, B, L, states, w_hard, ws, stream));
 }
 
+int64_t bcjr_code_words(const bcjr_trellis* tr, int64_t L) {
+  if (tr == nullptr || !shape_ok(tr) || tr->weights_per_step != 1 || L < 1) return 0;
+  return code_words(tr->state_bits, tr->bits_per_step, L);
+}
+
+bcjr_status bcjr_pack_code(const bcjr_trellis* tr, const int32_t* states, int64_t B, int64_t L,
+                           uint32_t* code, bcjr_stream_t stream) {
+  if (tr == nullptr) return BCJR_E_ARG;
+  if (!shape_ok(tr) || B < 0 || L < 1 || (B > 0 && L > ((int64_t)1 << 40) / B)) return BCJR_E_SHAPE;
+  if (tr->weights_per_step != 1) return BCJR_E_UNSUPPORTED;
+  if (B == 0) return BCJR_OK;
+  if (!states || !code) return BCJR_E_ARG;
+  return from_hip(launch_pack_code(tr->state_bits, tr->bits_per_step, states, B, L, code, stream));
+}
+
+bcjr_status bcjr_unpack_code(const bcjr_trellis* tr, const uint32_t* code, int64_t B, int64_t L,
+                             int32_t* states, float* w_hard, bcjr_stream_t stream) {
+  if (tr == nullptr) return BCJR_E_ARG;
+  if (!shape_ok(tr) || B < 0 || L < 1 || (B > 0 && L > ((int64_t)1 << 40) / B)) return BCJR_E_SHAPE;
+  if (tr->weights_per_step != 1) return BCJR_E_UNSUPPORTED;
+  if (B == 0) return BCJR_OK;
+  if (!code || !states || (w_hard && !tr->codebook)) return BCJR_E_ARG;
+  return from_hip(launch_unpack_code(tr->state_bits, tr->bits_per_step, code, B, L, tr->codebook,
+                                     states, w_hard, stream));
+}
+
 int bcjr_dense_supported(int32_t S) { return S >= 1 && S <= 65536 && dense_shape_built(S) ? 1 : 0; }
 
 size_t bcjr_dense_saved_bytes(int32_t S, int64_t B, int64_t L) {

@@ -89,6 +89,14 @@ int resident_grid(const void* kernel, int block, int64_t slots);
 int launch_viterbi(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                    int64_t L, int32_t* states, float* w_hard, void* ws, void* stream);
 
+// ---- hard-code export (bitshift trellis) -----------------------------------------------------
+// 32-bit words of one chain's code: n bits of the initial state + k bits per later step.
+inline int64_t code_words(int n, int k, int64_t L) { return ((int64_t)n + (int64_t)k * (L - 1) + 31) / 32; }
+int launch_pack_code(int n, int k, const int32_t* states, int64_t B, int64_t L, uint32_t* code,
+                     void* stream);
+int launch_unpack_code(int n, int k, const uint32_t* code, int64_t B, int64_t L,
+                       const float* codebook, int32_t* states, float* w_hard, void* stream);
+
 // ---- dense (fully connected) trellis -------------------------------------------------------
 // Sweep kernels use one persistent block per 4 chains, at most kDenseSweepMaxGrid blocks; the
 // theta-gradient product at most kDenseGemmMaxGrid blocks. Both bounds size workspace partials.

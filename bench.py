@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1536, help="chains timed on the CPU oracle")
     ap.add_argument("--cpu-sample-dense", type=int, default=64,
                     help="chains of the dense workload timed on the CPU oracle")
+    ap.add_argument("--export", action="store_true",
+                    help="time the hard-code export (pack / unpack of Viterbi paths) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -245,6 +247,61 @@ def bench_dense(args, wl):
     print(json.dumps(out))
 
 
+# Hard-code export: pack reads the int32 state path and writes k bits per step; unpack reads the
+# code (each word serves 32/k states through the caches) and writes the int32 states and the fp32
+# hard codeword. Algorithmic HBM bytes per chain-step: pack 4 + k/8, unpack k/8 + 8.
+PEAK_HBM = 8.0e12
+
+
+def bench_export(args, wl):
+    import numpy as np
+    import torch
+
+    from bcjr_soft_decoding_amd import bcjr, synth
+    n, k, B, L = wl.n, wl.k, wl.B, wl.L
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = torch.from_numpy(synth.codebook(wl.index)).to(dev)
+    w = torch.from_numpy(synth.weights(wl.index)).to(dev)
+    states, _ = bcjr.viterbi_decode(c, w, n, k, want_w_hard=False)
+    code = bcjr.bcjr_pack_code(states, n, k)
+    st2 = torch.empty_like(states)
+    wh2 = torch.empty_like(w)
+    for _ in range(args.warmup):
+        bcjr.bcjr_pack_code(states, n, k, code)
+        bcjr.bcjr_unpack_code(code, n, k, L, c, st2, wh2)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        bcjr.bcjr_pack_code(states, n, k, code)
+        e[1].record()
+        bcjr.bcjr_unpack_code(code, n, k, L, c, st2, wh2)
+        e[2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.equal(st2, states)
+    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    unpack_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    steps = B * L
+    pack_b, unpack_b = steps * (4 + k / 8), steps * (k / 8 + 8)
+    ach = unpack_b / (unpack_ms * 1e-3)
+    print(json.dumps({
+        "metric": "hard-code export chain-steps/sec (pack + unpack, 1 MI355X)",
+        "value": steps / (elapsed / args.steps), "unit": "chain-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "-viterbi-export", "B": B, "L": L, "S": wl.S, "k": k,
+                   "code_words_per_chain": int(code.shape[1]), "parallelism": "single-gpu"},
+        "kernels_ms": {"pack": pack_ms, "unpack": unpack_ms},
+        "roofline": {"bound": "hbm", "kernel": "k_unpack_code", "achieved": ach / 1e9,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": ach / PEAK_HBM,
+                     "pack_frac": pack_b / (pack_ms * 1e-3) / PEAK_HBM, "traffic": None},
+    }))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -262,6 +319,10 @@ def main():
     from bcjr_soft_decoding_amd import bcjr, synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.export:
+        if wl.dense:
+            raise SystemExit("the hard-code export is defined for the bitshift trellis")
+        return bench_export(args, wl)
     if wl.dense:
         return bench_dense(args, wl)
     T = args.temp if args.temp is not None else wl.temps[0]

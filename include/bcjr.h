@@ -134,6 +134,39 @@ bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, in
                            int32_t* states, float* w_hard, void* ws, size_t ws_bytes,
                            bcjr_stream_t stream);
 
+/* ---- Hard-code export (bitshift trellis) ------------------------------------------------------
+ * The zero-temperature end of the method: the hard code that the abstract says is recovered as
+ * T -> 0. A state path of the bitshift trellis is fixed by its first state and the k bits each
+ * step shifts in, s_t = ((s_{t-1} << k) | b_t) & (S-1), b_t = s_t mod K, so a chain's code is
+ * the bit string s_0 (n bits, most significant first) followed by b_1 .. b_{L-1} (k bits each,
+ * most significant first): n + k (L-1) bits in 32-bit words, the first bit in the most
+ * significant position of word 0, the tail of the last word zero (the pages give no packing;
+ * this is the reading). Every s_t is the n-bit window of the code starting at bit k t.
+ */
+
+/* 32-bit words per chain, ceil((n + k (L-1)) / 32); 0 for an invalid shape. Host only. */
+int64_t bcjr_code_words(const bcjr_trellis* tr, int64_t L);
+
+/*
+ * Pack state paths into codes.
+ * states DEVICE int32 [B,L], a path of the trellis (e.g. from viterbi_decode; a step whose state
+ *        is not a successor of the previous one keeps only its low k bits)
+ * code   DEVICE uint32 [B, bcjr_code_words(tr, L)] written
+ * The codebook pointer of tr is not used. Errors: BCJR_E_SHAPE, BCJR_E_ARG (null pointer with
+ * B > 0), BCJR_E_UNSUPPORTED (weights_per_step != 1). B = 0 enqueues nothing.
+ */
+bcjr_status bcjr_pack_code(const bcjr_trellis* tr, const int32_t* states, int64_t B, int64_t L,
+                           uint32_t* code, bcjr_stream_t stream);
+
+/*
+ * Unpack codes into state paths and, optionally, the hard codeword c(s_t).
+ * code   DEVICE uint32 [B, bcjr_code_words(tr, L)]
+ * states DEVICE int32 [B,L] written
+ * w_hard DEVICE [B,L] written with c(states), or NULL (then tr->codebook may be NULL)
+ */
+bcjr_status bcjr_unpack_code(const bcjr_trellis* tr, const uint32_t* code, int64_t B, int64_t L,
+                             int32_t* states, float* w_hard, bcjr_stream_t stream);
+
 /* ---- Dense (fully connected) trellis --------------------------------------------------------
  * Every state may follow every state; theta [S,S] (DEVICE, row-major, theta[s*S + s'] for the
  * transition s -> s') holds transition log-potentials. A path's weight is

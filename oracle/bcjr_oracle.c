@@ -459,6 +459,80 @@ int oracle_viterbi_f64(int n, int k, const float* c, const float* w, long B, lon
   VITERBI_BODY(double)
 }
 
+/* ---------------------------------------------------------------------------------------- */
+/* Hard-code export, the zero-temperature end of the method (abstract: the hard QTIP code is   */
+/* recovered as T -> 0). In the bitshift trellis a state path is fixed by its first state and  */
+/* the k bits every step shifts in: s_t = ((s_{t-1} << k) | b_t) & (S-1), b_t = s_t mod K.     */
+/* The code of a chain is the bit string s_0 (n bits, most significant first) followed by      */
+/* b_1, ..., b_{L-1} (k bits each, most significant first), n + k (L-1) bits in 32-bit words,  */
+/* the first bit in the most significant position of word 0 and the unused tail of the last   */
+/* word zero. (The pages do not give a packing; this is the reading.)                          */
+/* ---------------------------------------------------------------------------------------- */
+long oracle_code_words(int n, int k, long L) { return ((long)n + (long)k * (L - 1) + 31) / 32; }
+
+static void put_bits(uint32_t* words, long* pos, uint32_t value, int nbits) {
+  for (int i = nbits - 1; i >= 0; --i) {
+    const uint32_t bit = (value >> i) & 1u;
+    words[*pos / 32] |= bit << (31 - (int)(*pos % 32));
+    ++*pos;
+  }
+}
+
+static uint32_t get_bits(const uint32_t* words, long* pos, int nbits) {
+  uint32_t v = 0;
+  for (int i = 0; i < nbits; ++i) {
+    const uint32_t bit = (words[*pos / 32] >> (31 - (int)(*pos % 32))) & 1u;
+    v = (v << 1) | bit;
+    ++*pos;
+  }
+  return v;
+}
+
+/* Pack each chain's state path; *bad counts the steps whose state is not a successor of the   */
+/* previous one (such a path cannot be represented and packs to its successor-consistent code). */
+int oracle_pack_states(int n, int k, const int32_t* states, long B, long L, uint32_t* code,
+                       long* bad) {
+  if (n < 1 || n > 16 || k < 1 || k > n || B < 0 || L < 1) return -1;
+  const long W = oracle_code_words(n, k, L);
+  const uint32_t S = 1u << n, K = 1u << k;
+  long nbad = 0;
+  for (long q = 0; q < B; ++q) {
+    uint32_t* words = code + q * W;
+    for (long i = 0; i < W; ++i) words[i] = 0;
+    const int32_t* st = states + q * L;
+    long pos = 0;
+    put_bits(words, &pos, (uint32_t)st[0] & (S - 1), n);
+    for (long t = 1; t < L; ++t) {
+      const uint32_t prev = (uint32_t)st[t - 1], cur = (uint32_t)st[t];
+      if ((((prev << k) | (cur & (K - 1))) & (S - 1)) != cur) ++nbad;
+      put_bits(words, &pos, cur & (K - 1), k);
+    }
+  }
+  if (bad) *bad = nbad;
+  return 0;
+}
+
+/* Replay the shift register from the code; w_hard (may be NULL) gets c(s_t). */
+int oracle_unpack_code(int n, int k, const float* c, const uint32_t* code, long B, long L,
+                       int32_t* states, float* w_hard) {
+  if (n < 1 || n > 16 || k < 1 || k > n || B < 0 || L < 1) return -1;
+  const long W = oracle_code_words(n, k, L);
+  const uint32_t S = 1u << n;
+  for (long q = 0; q < B; ++q) {
+    const uint32_t* words = code + q * W;
+    long pos = 0;
+    uint32_t s = get_bits(words, &pos, n);
+    states[q * L] = (int32_t)s;
+    for (long t = 1; t < L; ++t) {
+      s = ((s << k) | get_bits(words, &pos, k)) & (S - 1);
+      states[q * L + t] = (int32_t)s;
+    }
+    if (w_hard)
+      for (long t = 0; t < L; ++t) w_hard[q * L + t] = c[states[q * L + t]];
+  }
+  return 0;
+}
+
 /* Thread count used by the OpenMP loops (the CPU baseline reports it). */
 int oracle_set_threads(int nthreads) {
 #ifdef _OPENMP

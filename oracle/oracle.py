@@ -45,9 +45,13 @@ def _load():
     lib.oracle_viterbi_f32.argtypes = [I, I, P, P, Lg, Lg, P, P, P]
     lib.oracle_viterbi_f64.argtypes = [I, I, P, P, Lg, Lg, P, P, P]
     lib.oracle_set_threads.argtypes = [I]
+    lib.oracle_code_words.argtypes = [I, I, Lg]
+    lib.oracle_code_words.restype = Lg
+    lib.oracle_pack_states.argtypes = [I, I, P, Lg, Lg, P, P]
+    lib.oracle_unpack_code.argtypes = [I, I, P, P, Lg, Lg, P, P]
     for name in ("oracle_sparse_forward", "oracle_sparse_backward", "oracle_dense_forward",
                  "oracle_dense_backward", "oracle_viterbi_f32", "oracle_viterbi_f64",
-                 "oracle_set_threads"):
+                 "oracle_set_threads", "oracle_pack_states", "oracle_unpack_code"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -151,3 +155,30 @@ def viterbi(n, k, codebook, w, precision="f32"):
     fn = lib.oracle_viterbi_f32 if precision == "f32" else lib.oracle_viterbi_f64
     _check(fn(n, k, _p(c), _p(w), B, L, _p(states), _p(w_hard), _p(energy)), "viterbi")
     return {"states": states, "w_hard": w_hard, "energy": energy}
+
+
+def code_words(n: int, k: int, L: int) -> int:
+    return int(_load().oracle_code_words(n, k, L))
+
+
+def pack_states(n, k, states):
+    """Hard code of every chain: uint32 [B, words]; also the number of non-successor steps."""
+    lib = _load()
+    st = np.ascontiguousarray(states, dtype=np.int32)
+    B, L = st.shape
+    code = np.zeros((B, code_words(n, k, L)), np.uint32)
+    bad = ctypes.c_long(0)
+    _check(lib.oracle_pack_states(n, k, _p(st), B, L, _p(code), ctypes.byref(bad)), "pack_states")
+    return code, int(bad.value)
+
+
+def unpack_code(n, k, codebook, code, L):
+    """States int32 [B, L] and w_hard = c(states) fp32 [B, L] from the hard code."""
+    lib = _load()
+    c = _f32(codebook)
+    cd = np.ascontiguousarray(code, dtype=np.uint32)
+    B = cd.shape[0]
+    states = np.empty((B, L), np.int32)
+    w_hard = np.empty((B, L), np.float32)
+    _check(lib.oracle_unpack_code(n, k, _p(c), _p(cd), B, L, _p(states), _p(w_hard)), "unpack_code")
+    return states, w_hard

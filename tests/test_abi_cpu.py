@@ -209,3 +209,20 @@ def test_checkpointed_workspace_sizes(lib):
     assert f > 200 * 2**30 and c < 16 * 2**30
     assert bcjr.bcjr_workspace_bytes(8, 2, 16, 16, 5) == 0
     assert bcjr.bcjr_workspace_bytes(8, 2, 0, 16, bcjr.BWD_CKPT) == 0
+
+
+def test_code_export_queries_and_validation(lib):
+    import oracle
+    for n, k, L in [(4, 2, 1), (8, 2, 256), (16, 2, 256), (12, 3, 100), (16, 1, 4096)]:
+        assert bcjr.bcjr_code_words(n, k, L) == oracle.code_words(n, k, L)
+    assert bcjr.bcjr_code_words(17, 2, 10) == 0
+    assert bcjr.bcjr_code_words(8, 2, 0) == 0
+    P = ctypes.c_void_p
+    tr = bcjr.Trellis(8, 2, 1, 0)
+    assert lib.bcjr_pack_code(ctypes.byref(tr), None, 4, 8, P(0x1000), None) == bcjr.BCJR_E_ARG
+    assert lib.bcjr_pack_code(ctypes.byref(tr), P(0x1000), -1, 8, P(0x1000), None) == bcjr.BCJR_E_SHAPE
+    assert lib.bcjr_pack_code(ctypes.byref(tr), None, 0, 8, None, None) == bcjr.BCJR_OK
+    # w_hard needs the codebook
+    assert lib.bcjr_unpack_code(ctypes.byref(tr), P(0x1000), 4, 8, P(0x2000), P(0x3000), None) == bcjr.BCJR_E_ARG
+    tr2 = bcjr.Trellis(8, 2, 2, 0x4000)
+    assert lib.bcjr_unpack_code(ctypes.byref(tr2), P(0x1000), 4, 8, P(0x2000), None, None) == bcjr.BCJR_E_UNSUPPORTED
