@@ -13,13 +13,17 @@
 
 namespace bcjr {
 
-enum Kind { kFwd = 0, kBwd = 1, kVit = 2 };
+// kFwd / kBwd: forward and backward with fp32 messages; kFwdP / kBwdP: the same kernels with
+// fp64 messages (twice the message registers, so fewer states per lane); kVit: Viterbi.
+enum Kind { kFwd = 0, kBwd = 1, kVit = 2, kFwdP = 3, kBwdP = 4 };
 
 constexpr int kMaxLanesPerChain = 1024;
 
 // States per lane each kernel aims for (more states per lane: fewer lanes per chain, cheaper
 // per-step exchanges and reductions, more registers). Measured on MI355X at S = 4096.
-constexpr int geom_target_states(int kind) { return kind == kFwd ? 64 : kind == kBwd ? 32 : 16; }
+constexpr int geom_target_states(int kind) {
+  return kind == kFwd ? 64 : kind == kBwd ? 32 : kind == kFwdP ? 32 : 16;
+}
 
 // Kernels are built for k in {1, 2, 3} and 2k <= n <= 16, except where the two backward
 // messages of one chain (2 * S/K floats, single-buffered) would not fit the 160 KiB of LDS.

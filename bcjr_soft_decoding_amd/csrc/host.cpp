@@ -22,6 +22,7 @@ bool sparse_geom(int n, int k, int64_t B, int kind, SparseGeom* g) {
   g->LPS = geom_lps(n, k, kind);
   g->SPB = geom_spb(n, k, kind);
   g->BLOCK = geom_block(n, k, kind);
+  g->B = B;
   g->units = B > 0 ? (B + g->SPB - 1) / g->SPB : 0;
   const int64_t mx = geom_max_slots(n, k, kind);
   g->slots = g->units < mx ? g->units : mx;
@@ -40,12 +41,33 @@ int resident_grid(const void* kernel, int block, int64_t slots) {
   return (int)(slots < cap ? slots : cap);
 }
 
-size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+namespace {
+size_t fwd_ws_one(const SparseGeom& g, int64_t L, bool ckpt) {
   return (size_t)g.slots * sparse_fwd_slot_bytes(g, L, ckpt);
 }
-size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+size_t bwd_ws_one(const SparseGeom& g, int64_t L, bool ckpt) {
   return (size_t)g.slots * sparse_bwd_slot_bytes(g, L, ckpt) +
          round256((size_t)g.slots * g.S * sizeof(float));
+}
+}  // namespace
+
+size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+  size_t need = fwd_ws_one(g, L, ckpt);
+  SparseGeom p;
+  if (sparse_geom(g.n, g.k, g.B, kFwdP, &p)) {
+    const size_t q = fwd_ws_one(p, L, ckpt);
+    if (q > need) need = q;
+  }
+  return need;
+}
+size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
+  size_t need = bwd_ws_one(g, L, ckpt);
+  SparseGeom p;
+  if (sparse_geom(g.n, g.k, g.B, kBwdP, &p)) {
+    const size_t q = bwd_ws_one(p, L, ckpt);
+    if (q > need) need = q;
+  }
+  return need;
 }
 size_t sparse_vit_ws_bytes(const SparseGeom& g, int64_t L) {
   return round256((size_t)g.slots * L * g.BLOCK * (g.K * g.G));

@@ -22,6 +22,7 @@ struct SparseGeom {
   int LPS;       // lanes per chain
   int SPB;       // chains per block (LPS < 64: 64 / LPS, else 1)
   int BLOCK;     // threads per block
+  int64_t B;     // chains
   int64_t units; // ceil(B / SPB)
   int64_t slots; // workspace slots = the most blocks a launch may use
 };
@@ -69,6 +70,8 @@ inline size_t sparse_bwd_slot_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
   return round256((size_t)sparse_hist_entries(L, ckpt) * g.BLOCK * (g.K * g.G) * 12 +
                   (size_t)L * g.SPB * 8);
 }
+// Forward / backward workspace for the fp32-message geometry g: enough for either message
+// precision (the fp64-message kernels run with the kFwdP / kBwdP geometry of the same n, k, B).
 size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt);
 size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt);
 size_t sparse_vit_ws_bytes(const SparseGeom& g, int64_t L);

@@ -832,12 +832,18 @@ k_reduce_slots(const float* __restrict__ partial, long long slots, long long cou
 }
 
 // Messages are carried in fp64 below this temperature, for every shape whose backward
-// message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS.
+// message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS. The fp64-message
+// kernels use their own lane geometry (kFwdP / kBwdP): fewer states per lane, since every
+// message takes two registers.
 constexpr float kPreciseBelowT = 0.05f;
 template <int n, int k>
 constexpr bool precise_fits() {
-  return (long long)geom_spb(n, k, kBwd) * ((1LL << n) >> k) * 12 <= 150 * 1024;
+  return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;
 }
+template <class P>
+constexpr int fwd_kind() { return P::kPrecise ? kFwdP : kFwd; }
+template <class P>
+constexpr int bwd_kind() { return P::kPrecise ? kBwdP : kBwd; }
 template <int n, int k>
 bool use_precise(float T) {
   return precise_fits<n, k>() && T < kPreciseBelowT;
@@ -862,8 +868,9 @@ template <int n, int k, class P>
 int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, float* w_hat, float* log_z, float* saved, void* ws, bool ckpt,
               hipStream_t st) {
-  using C = Cfg<(1 << k), geom_g(n, k, kFwd), geom_lps(n, k, kFwd), P, false>;
+  using C = Cfg<(1 << k), geom_g(n, k, fwd_kind<P>()), geom_lps(n, k, fwd_kind<P>()), P, false>;
   static_assert(C::S == (1 << n), "geometry mismatch");
+  if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
   const Consts kc = make_consts(T, P::kPrecise);
   const size_t slot = sparse_fwd_slot_bytes(g, L, ckpt);
   const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
@@ -886,8 +893,9 @@ template <int n, int k, class P>
 int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, const float* saved, const float* gup, const float* hup, float* grad_w,
               float* grad_c, void* ws, bool ckpt, hipStream_t st) {
-  using C = Cfg<(1 << k), geom_g(n, k, kBwd), geom_lps(n, k, kBwd), P, true>;
+  using C = Cfg<(1 << k), geom_g(n, k, bwd_kind<P>()), geom_lps(n, k, bwd_kind<P>()), P, true>;
   static_assert(C::S == (1 << n), "geometry mismatch");
+  if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
   const Consts kc = make_consts(T, P::kPrecise);
   const size_t slot = sparse_bwd_slot_bytes(g, L, ckpt);
   const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
@@ -918,8 +926,11 @@ int run_fwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
             float T, float* w_hat, float* log_z, float* saved, void* ws, bool ckpt,
             hipStream_t st) {
   if constexpr (precise_fits<n, k>())
-    if (use_precise<n, k>(T))
-      return run_fwd_p<n, k, Precise>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+    if (use_precise<n, k>(T)) {
+      SparseGeom gp;
+      if (!sparse_geom(n, k, B, kFwdP, &gp)) return (int)hipErrorInvalidValue;
+      return run_fwd_p<n, k, Precise>(gp, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+    }
   return run_fwd_p<n, k, Fast>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
 }
 
@@ -928,9 +939,12 @@ int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
             float T, const float* saved, const float* gup, const float* hup, float* grad_w,
             float* grad_c, void* ws, bool ckpt, hipStream_t st) {
   if constexpr (precise_fits<n, k>())
-    if (use_precise<n, k>(T))
-      return run_bwd_p<n, k, Precise>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt,
-                                      st);
+    if (use_precise<n, k>(T)) {
+      SparseGeom gp;
+      if (!sparse_geom(n, k, B, kBwdP, &gp)) return (int)hipErrorInvalidValue;
+      return run_bwd_p<n, k, Precise>(gp, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws,
+                                      ckpt, st);
+    }
   return run_bwd_p<n, k, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt, st);
 }
 

@@ -101,3 +101,20 @@ def normal(seed: int, shape, scale: float = 1.0) -> np.ndarray:
     if scale != 1.0:
         x = (x * np.float32(scale)).astype(np.float32)
     return x
+
+
+def qat_layer(rows: int, cols: int, samples: int, n: int, seed: int = 0):
+    """One synthetic linear layer for the annealed-QAT driver, all fp32 numpy:
+    float weights W [rows, cols] rescaled to unit RMS, calibration and held-out inputs
+    X, Xv [samples, cols], codebook c [2^n] ~ N(0,1).
+
+    Inputs carry per-channel scales exp(0.75 xi), xi ~ N(0,1): a log-normal spread like the
+    outlier channels of LLM activations, so the output error weighs weights unequally.
+    Seeds 9000+seed (W), 9100+seed (scales), 9200+seed (X), 9300+seed (Xv), 9400+seed (c)."""
+    W = _normal(9000 + seed, (rows, cols)).astype(np.float64)
+    W = (W / np.sqrt(np.mean(W * W))).astype(np.float32)
+    scale = np.exp(0.75 * _normal(9100 + seed, (cols,)).astype(np.float64))
+    X = (_normal(9200 + seed, (samples, cols)) * scale).astype(np.float32)
+    Xv = (_normal(9300 + seed, (samples, cols)) * scale).astype(np.float32)
+    c = _normal(9400 + seed, (1 << n,))
+    return W, X, Xv, c

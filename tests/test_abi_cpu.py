@@ -226,3 +226,19 @@ def test_code_export_queries_and_validation(lib):
     assert lib.bcjr_unpack_code(ctypes.byref(tr), P(0x1000), 4, 8, P(0x2000), P(0x3000), None) == bcjr.BCJR_E_ARG
     tr2 = bcjr.Trellis(8, 2, 2, 0x4000)
     assert lib.bcjr_unpack_code(ctypes.byref(tr2), P(0x1000), 4, 8, P(0x2000), None, None) == bcjr.BCJR_E_UNSUPPORTED
+
+
+def test_qat_driver_validates_before_any_gpu_call():
+    import torch
+    from bcjr_soft_decoding_amd import qat
+    W = torch.zeros(2, 512)
+    with pytest.raises(TypeError):
+        qat.train(W, torch.zeros(4, 512), torch.zeros(256), qat.QATConfig(n=8, steps=1))
+    with pytest.raises(ValueError):
+        qat.train(W, torch.zeros(4, 512), torch.zeros(256), qat.QATConfig(n=8, L=300))
+    with pytest.raises(ValueError):
+        qat.QATConfig(t0=0.0).check()
+    with pytest.raises(ValueError):
+        qat.QATConfig(n=3, k=2).check()
+    cfg = qat.QATConfig(t0=0.3, t_end=0.01, steps=5)
+    assert qat.temperature(cfg, 0) == pytest.approx(0.3) and qat.temperature(cfg, 4) == pytest.approx(0.01)
