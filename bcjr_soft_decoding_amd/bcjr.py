@@ -23,6 +23,7 @@ EXPORTED = (
     "bcjr_backward", "viterbi_decode", "bcjr_dense_supported", "bcjr_dense_saved_bytes",
     "bcjr_dense_workspace_bytes", "bcjr_dense_forward", "bcjr_dense_backward",
     "bcjr_code_words", "bcjr_pack_code", "bcjr_unpack_code", "bcjr_status_string",
+    "bcjr_scan_segment_length", "bcjr_scan_workspace_bytes", "bcjr_forward_scan",
 )
 
 
@@ -83,6 +84,12 @@ def lib() -> ctypes.CDLL:
     L.bcjr_pack_code.restype = ctypes.c_int
     L.bcjr_unpack_code.argtypes = [TP, P, I64, I64, P, P, P]
     L.bcjr_unpack_code.restype = ctypes.c_int
+    L.bcjr_scan_segment_length.argtypes = [TP, I64, I64, I64]
+    L.bcjr_scan_segment_length.restype = I64
+    L.bcjr_scan_workspace_bytes.argtypes = [TP, I64, I64, I64]
+    L.bcjr_scan_workspace_bytes.restype = SZ
+    L.bcjr_forward_scan.argtypes = [TP, P, I64, I64, F, I64, P, P, P, SZ, P]
+    L.bcjr_forward_scan.restype = ctypes.c_int
     L.bcjr_status_string.argtypes = [ctypes.c_int]
     L.bcjr_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -153,6 +160,33 @@ def bcjr_forward(codebook, w, n, k, T, w_hat=None, log_z=None, saved=None, ws=No
                             _ptr(saved), _ptr(ws), ws.numel(), _stream())
     _check(st, "bcjr_forward")
     return w_hat, log_z, saved
+
+
+def bcjr_scan_segment_length(n: int, k: int, B: int, L: int, seg_len: int = 0) -> int:
+    tr = trellis(n, k)
+    return int(lib().bcjr_scan_segment_length(ctypes.byref(tr), B, L, seg_len))
+
+
+def bcjr_scan_workspace_bytes(n: int, k: int, B: int, L: int, seg_len: int = 0) -> int:
+    tr = trellis(n, k)
+    return int(lib().bcjr_scan_workspace_bytes(ctypes.byref(tr), B, L, seg_len))
+
+
+def bcjr_forward_scan(codebook, w, n, k, T, seg_len=0, w_hat=None, log_z=None, ws=None):
+    """Segmented (parallel-in-L) forward for few, long chains; returns (w_hat, log_z)."""
+    _f32(codebook, "codebook"); _f32(w, "w")
+    B, L = w.shape
+    dev = w.device
+    w_hat = torch.empty_like(w) if w_hat is None else w_hat
+    log_z = torch.empty(B, dtype=torch.float32, device=dev) if log_z is None else log_z
+    if ws is None:
+        nb = bcjr_scan_workspace_bytes(n, k, B, L, seg_len)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    tr = trellis(n, k, codebook)
+    st = lib().bcjr_forward_scan(ctypes.byref(tr), _ptr(w), B, L, float(T), int(seg_len),
+                                 _ptr(w_hat), _ptr(log_z), _ptr(ws), ws.numel(), _stream())
+    _check(st, "bcjr_forward_scan")
+    return w_hat, log_z
 
 
 def bcjr_backward(codebook, w, n, k, T, saved, grad_w_hat, grad_log_z=None, grad_w=None,

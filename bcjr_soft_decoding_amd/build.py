@@ -28,7 +28,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-result", "-Wno-unknown-pragmas",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kernels.hip", "code_kernels.hip"]
+SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kernels.hip", "code_kernels.hip",
+           "scan_kernels.hip"]
 # The forward-backward kernels assume finite inputs (NaN in w, the codebook or theta gives
 # unspecified outputs), so their max reductions need no NaN canonicalisation; the Viterbi
 # decoder keeps strict IEEE semantics for its bit-exact contract.

@@ -126,9 +126,93 @@ bcjr_status dense_check(int32_t S, int64_t B, int64_t L) {
   return BCJR_OK;
 }
 
+// Segmented forward: validation shared by the size queries and the call (no device use).
+bcjr_status scan_setup(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len,
+                       ScanPlan* plan) {
+  if (tr == nullptr) return BCJR_E_ARG;
+  if (!shape_ok(tr) || B < 0 || L < 1) return BCJR_E_SHAPE;
+  if (tr->weights_per_step != 1) return BCJR_E_UNSUPPORTED;
+  if (seg_len < 0) return BCJR_E_ARG;
+  const int n = tr->state_bits, k = tr->bits_per_step;
+  if (!scan_shape_built(n, k)) return BCJR_E_UNSUPPORTED;
+  const int64_t M = ((int64_t)1 << n) >> k;
+  if (B > ((int64_t)1 << 40) / L) return BCJR_E_SHAPE;
+  const int64_t seg = seg_len > 0 ? seg_len : scan_default_seg(n, k, B, L);
+  const int64_t s_eff = seg < L ? seg : L;
+  const int64_t pmain = L / s_eff;
+  const int64_t ptot = pmain + (L % s_eff ? 1 : 0);
+  if (B > 0 && ptot > ((int64_t)1 << 58) / (B * M * M * 4)) return BCJR_E_SHAPE;
+  SparseGeom gm, gt;
+  if (!sparse_geom(n, k, B * pmain, kFwd, &gm) || !sparse_geom(n, k, B, kFwd, &gt))
+    return BCJR_E_UNSUPPORTED;
+  scan_plan(gm, gt, n, k, B, L, seg, plan);
+  return BCJR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t bcjr_scan_segment_length(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len) {
+  ScanPlan plan;
+  if (scan_setup(tr, B, L, seg_len, &plan) != BCJR_OK) return 0;
+  return plan.seg;
+}
+
+size_t bcjr_scan_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len) {
+  ScanPlan plan;
+  if (scan_setup(tr, B, L, seg_len, &plan) != BCJR_OK || B == 0) return 0;
+  return plan.bytes;
+}
+
+bcjr_status bcjr_forward_scan(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                              float T, int64_t seg_len, float* w_hat, float* log_z, void* ws,
+                              size_t ws_bytes, bcjr_stream_t stream) {
+  ScanPlan plan;
+  bcjr_status st = scan_setup(tr, B, L, seg_len, &plan);
+  if (st != BCJR_OK) return st;
+  if (!temp_ok(T)) return BCJR_E_ARG;
+  if (B == 0) return BCJR_OK;
+  if (!w || !w_hat || !log_z || tr->codebook == nullptr) return BCJR_E_ARG;
+  if (!ws_ok(ws, ws_bytes, plan.bytes)) return BCJR_E_WORKSPACE;
+  const int n = tr->state_bits, k = tr->bits_per_step;
+  const int M = (1 << n) >> k;
+  char* base = static_cast<char*>(ws);
+  float* rows = reinterpret_cast<float*>(base + plan.rows);
+  double* rscale = reinterpret_cast<double*>(base + plan.rscale);
+  double* lam0 = reinterpret_cast<double*>(base + plan.lam0);
+  double* rho1 = reinterpret_cast<double*>(base + plan.rho1);
+  double* sc0 = reinterpret_cast<double*>(base + plan.sc0);
+  void* slots = base + plan.slots;
+  int e = 0;
+  // phase 1: transfer rows of every segment (not needed for a single segment)
+  if (plan.ptot > 1) {
+    SegLaunch sl{plan.pmain, 0, plan.seg, L, plan.ptot, nullptr, nullptr, nullptr, rows, rscale};
+    e = launch_sparse_forward_seg(2, n, k, tr->codebook, w, B * plan.pmain * M, plan.seg, T,
+                                  nullptr, nullptr, slots, sl, stream);
+    if (e == 0 && plan.tail > 0) {
+      sl.nseg = 1;
+      sl.jbase = plan.pmain;
+      e = launch_sparse_forward_seg(2, n, k, tr->codebook, w, B * M, plan.tail, T, nullptr,
+                                    nullptr, slots, sl, stream);
+    }
+  }
+  // phase 2: boundary messages by a scan over the segments
+  if (e == 0) e = launch_scan_bounds(rows, rscale, B, plan.ptot, M, lam0, rho1, sc0, stream);
+  // phase 3: every segment's forward-backward from its boundary messages
+  if (e == 0) {
+    SegLaunch sl{plan.pmain, 0, plan.seg, L, plan.ptot, lam0, rho1, sc0, nullptr, nullptr};
+    e = launch_sparse_forward_seg(1, n, k, tr->codebook, w, B * plan.pmain, plan.seg, T, w_hat,
+                                  log_z, slots, sl, stream);
+    if (e == 0 && plan.tail > 0) {
+      sl.nseg = 1;
+      sl.jbase = plan.pmain;
+      e = launch_sparse_forward_seg(1, n, k, tr->codebook, w, B, plan.tail, T, w_hat, log_z,
+                                    slots, sl, stream);
+    }
+  }
+  return from_hip(e);
+}
 
 int bcjr_supported(const bcjr_trellis* tr) {
   if (tr == nullptr || !shape_ok(tr) || tr->weights_per_step != 1) return 0;

@@ -92,6 +92,85 @@ int resident_grid(const void* kernel, int block, int64_t slots);
 int launch_viterbi(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                    int64_t L, int32_t* states, float* w_hard, void* ws, void* stream);
 
+// ---- segmented forward of long chains (parallel in L) ---------------------------------------
+// A chain of L steps is cut into pmain segments of seg steps plus, if L is not a multiple, one
+// tail segment (ptot segments in all). Phase 1 computes every segment's M x M transfer matrix
+// (M = S/K) from M one-hot starts, phase 2 scans the boundary messages over the segments,
+// phase 3 runs the forward-backward of all segments at once from their boundary messages.
+struct SegLaunch {
+  int64_t nseg, jbase, seglen, lfull, ptot;
+  const double* lam0;
+  const double* rho1;
+  const double* sc0;
+  float* rows;
+  double* rscale;
+};
+// mode 2: transfer rows (Bv = chains * segments * M virtual chains); mode 1: segments with
+// boundary messages (Bv = chains * segments).
+int launch_sparse_forward_seg(int mode, int n, int k, const float* codebook, const float* w,
+                              int64_t Bv, int64_t L, float T, float* w_hat, float* log_z, void* ws,
+                              const SegLaunch& sl, void* stream);
+bool scan_shape_built(int n, int k);
+int launch_scan_bounds(const float* rows, const double* rscale, int64_t chains, int64_t ptot, int M,
+                       double* lam0, double* rho1, double* sc0, void* stream);
+
+constexpr int64_t kScanMinSeg = 16;
+
+// Default segment length. A chain's time is about P * t2 (the boundary scan, sequential over
+// its P = L / seg segments) + seg * t3 (each segment's own sweeps, sequential in its steps),
+// smallest at seg = sqrt(L * t2 / t3). Measured on MI355X: t3 = 3.2 us per step (forward and
+// backward sweep of one chain), t2 = 2.5 us + 3.7e-4 us * M^2 per scan step (M = S/K).
+// A segment shorter than the others (when seg does not divide L) runs in launches of its own
+// after the others, so the default prefers a divisor of L within 1.5x of that optimum, else
+// seg = floor(L / P) for P = ceil(L / optimum), which keeps the short segment under P steps.
+inline int64_t scan_default_seg(int n, int k, int64_t B, int64_t L) {
+  (void)B;
+  const double M = (double)(((int64_t)1 << n) >> k);
+  const double t2 = 2.5 + 3.7e-4 * M * M, t3 = 3.2;
+  const double opt = sqrt((double)L * t2 / t3);
+  if (opt <= (double)kScanMinSeg) return kScanMinSeg;
+  if (opt >= (double)L) return L;
+  const int64_t lo = (int64_t)ceil(opt / 1.5), hi = (int64_t)floor(opt * 1.5);
+  int64_t best = 0;
+  double best_r = 0.0;
+  for (int64_t d = lo < kScanMinSeg ? kScanMinSeg : lo; d <= hi && d <= L; ++d) {
+    if (L % d) continue;
+    const double r = d > opt ? d / opt : opt / d;
+    if (best == 0 || r < best_r) { best = d; best_r = r; }
+  }
+  if (best) return best;
+  const int64_t P = (int64_t)ceil((double)L / opt);
+  const int64_t seg = L / P;
+  return seg < kScanMinSeg ? kScanMinSeg : seg;
+}
+
+struct ScanPlan {
+  int64_t seg, pmain, tail, ptot;
+  size_t rows, rscale, lam0, rho1, sc0, slots, bytes;  // workspace offsets and total
+};
+
+inline void scan_plan(const SparseGeom& gmain, const SparseGeom& gtail, int n, int k, int64_t B,
+                      int64_t L, int64_t seg, ScanPlan* p) {
+  const int64_t M = ((int64_t)1 << n) >> k;
+  p->seg = seg < L ? seg : L;
+  p->pmain = L / p->seg;
+  p->tail = L - p->pmain * p->seg;
+  p->ptot = p->pmain + (p->tail > 0 ? 1 : 0);
+  const size_t cp = (size_t)B * (size_t)p->ptot;
+  p->rows = 0;
+  p->rscale = p->ptot > 1 ? round256(cp * (size_t)M * (size_t)M * sizeof(float)) : 0;
+  p->lam0 = p->rscale + (p->ptot > 1 ? round256(cp * (size_t)M * sizeof(double)) : 0);
+  p->rho1 = p->lam0 + round256(cp * (size_t)M * sizeof(double));
+  p->sc0 = p->rho1 + round256(cp * (size_t)M * sizeof(double));
+  p->slots = p->sc0 + round256(cp * 2 * sizeof(double));
+  size_t a = sparse_fwd_ws_bytes(gmain, p->seg, false);
+  if (p->tail > 0) {
+    const size_t b = sparse_fwd_ws_bytes(gtail, p->tail, false);
+    if (b > a) a = b;
+  }
+  p->bytes = p->slots + round256(a);
+}
+
 // ---- hard-code export (bitshift trellis) -----------------------------------------------------
 // 32-bit words of one chain's code: n bits of the initial state + k bits per later step.
 inline int64_t code_words(int n, int k, int64_t L) { return ((int64_t)n + (int64_t)k * (L - 1) + 31) / 32; }

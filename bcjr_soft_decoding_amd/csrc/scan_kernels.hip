@@ -1,0 +1,211 @@
+// Boundary messages of the segmented forward for long chains (parallel in L).
+//
+// The bitshift trellis's butterfly messages obey lam_{t+1} = lam_t (x) A_t and
+// rho_t = A_{t+1} (x) rho_{t+1} in the (log-sum-exp, +) semiring, one M x M matrix A_t per step
+// (the transfer-matrix view of the BCJR-QAT abstract). A chain cut into segments j = 0..P-1
+// with transfer matrices Q_j (rows from k_sparse_fwd's transfer-row mode) has
+//   lam at the start of segment j+1  = lam at the start of segment j (x) Q_j,   lam_0 = 0,
+//   rho at the end of segment j-1    = Q_j (x) rho at the end of segment j,    rho_{P-1} = 0
+// (free start and free end). k_scan_bounds runs these two scans, one block per chain and
+// direction, sequentially over the segments, and stores every boundary vector normalised by
+// the integer floor of its maximum together with that scale, the form the segment kernels take.
+//
+// Q_j arrives as fp32 row offsets Qn(i, .) <= 0 plus a double row scale rs(i):
+// Q(i, j) = rs(i) + Qn(i, j) (log2). Vectors and scales are double; each log-sum-exp is formed
+// against its own maximum with fp32 exponentials, so only offsets below the maximum are
+// rounded to fp32. Row tiles of Q_j are staged through LDS (padded stride), the next tile
+// being loaded into registers while the current one is reduced; every output's reduction is
+// split over 256/M threads (adjacent lanes, combined with shuffles).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace bcjr {
+namespace {
+
+constexpr int kScanBlock = 256;
+constexpr int kTileFloats = 8192;                           // one staged tile of Q rows
+constexpr int kTileVec = kTileFloats / 4 / kScanBlock;      // float4 loads per thread
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ double block_max(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int i = 1; i < kScanBlock / 64; ++i) r = fmax(r, red[i]);
+  return r;
+}
+
+// Running log-sum-exp (max m, sum s relative to m) merged with another.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * ex2(m - mn) + s2 * ex2(m2 - mn);
+  m = mn;
+}
+
+// Combine the partial (m, s) of the `width` adjacent lanes that share an output.
+__device__ __forceinline__ void group_lse(float& m, float& s, int width) {
+  for (int o = 1; o < width; o <<= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    lse_merge(m, s, m2, s2);
+  }
+}
+
+// rows: [chains][ptot][M][M] fp32 offsets; rscale: [chains][ptot][M];
+// lam0, rho1: [chains][ptot][M]; sc0: [chains][ptot][2]. R rows per tile, R * M <= kTileFloats.
+__global__ void __launch_bounds__(kScanBlock)
+k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale, long long ptot,
+              int M, int R, double* __restrict__ lam0, double* __restrict__ rho1,
+              double* __restrict__ sc0) {
+  extern __shared__ __attribute__((aligned(16))) double smd[];
+  const int RS = M + 4;  // padded tile row stride (keeps 16-byte alignment)
+  double* va = smd;                                  // current boundary vector [M]
+  double* vb = va + M;                               // next one [M]
+  double* rsd = vb + M;                              // row scales of the segment [M]
+  double* red = rsd + M;                             // reduction scratch [4]
+  float* vf = reinterpret_cast<float*>(red + 4);     // fp32 relative vector [M]
+  float* tile = vf + M;                              // [R][RS]
+  const long long c = blockIdx.x;
+  const bool fwd = blockIdx.y == 0;
+  const int tid = threadIdx.x;
+  const int ntile = M / R;
+  const long long nstep = ptot - 1;  // matrix-vector steps of the scan
+  for (int i = tid; i < M; i += kScanBlock) va[i] = 0.0;
+
+  // segment of scan step q: forward Q_q, backward Q_{ptot-1-q}
+  auto seg_of = [&](long long q) { return c * ptot + (fwd ? q : ptot - 1 - q); };
+  const int nv = R * M / 4;  // float4 vectors per tile
+  // Prefetch registers: tile u of scan step q (lanes past the tile reload its first vector) and,
+  // with tile 0, the thread's share of the segment's row scales (rows tid + 256 x).
+  float4 rv[kTileVec];
+  double rr[4];
+#define BCJR_LOAD_TILE(Q_, U_)                                                              \
+  do {                                                                                      \
+    const long long sg_ = seg_of(Q_);                                                       \
+    const float4* src_ =                                                                    \
+        reinterpret_cast<const float4*>(rows + (sg_ * M + (long long)(U_) * R) * M);        \
+    _Pragma("unroll") for (int v_ = 0; v_ < kTileVec; ++v_) {                               \
+      const int f_ = tid + v_ * kScanBlock;                                                 \
+      rv[v_] = src_[f_ < nv ? f_ : 0];                                                      \
+    }                                                                                       \
+    if ((U_) == 0) {                                                                        \
+      _Pragma("unroll") for (int x_ = 0; x_ < 4; ++x_) {                                    \
+        const int i_ = tid + x_ * kScanBlock;                                               \
+        rr[x_] = rscale[sg_ * M + (i_ < M ? i_ : 0)];                                       \
+      }                                                                                     \
+    }                                                                                       \
+  } while (0)
+  auto store_normalised = [&](const double* v, long long sg, double* out, double* scale) {
+    double m = -INFINITY;
+    for (int i = tid; i < M; i += kScanBlock) m = fmax(m, v[i]);
+    const double sh = floor(block_max(m, red));
+    for (int i = tid; i < M; i += kScanBlock) out[sg * M + i] = v[i] - sh;
+    if (tid == 0) *scale = sh;
+  };
+
+  // thread roles: forward output o = tid / tpo with rows ch, ch + tpo, ...; M > 256 loops outputs
+  const int tpo = M >= kScanBlock ? 1 : kScanBlock / M;
+  const int tpr = kScanBlock / R;  // backward: threads per row of a tile (R <= 256)
+#pragma unroll
+  for (int v = 0; v < kTileVec; ++v) rv[v] = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < 4; ++x) rr[x] = 0.0;
+  if (nstep > 0) BCJR_LOAD_TILE(0, 0);
+  for (long long q = 0;; ++q) {
+    const long long sgb = c * ptot + (fwd ? q : ptot - 1 - q);  // boundary this vector belongs to
+    __syncthreads();
+    store_normalised(va, sgb, fwd ? lam0 : rho1, sc0 + sgb * 2 + (fwd ? 0 : 1));
+    if (q == nstep) break;
+
+    // row scales of this step's segment, and the fp32 relative input vector
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      if (tid + x * kScanBlock < M) rsd[tid + x * kScanBlock] = rr[x];
+    __syncthreads();
+    double m_in = -INFINITY;
+    for (int i = tid; i < M; i += kScanBlock) m_in = fmax(m_in, fwd ? va[i] + rsd[i] : va[i]);
+    m_in = block_max(m_in, red);
+    for (int i = tid; i < M; i += kScanBlock)
+      vf[i] = (float)((fwd ? va[i] + rsd[i] : va[i]) - m_in);
+
+    float pm[4], ps[4];  // forward partials for up to 4 outputs (M <= 1024)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { pm[x] = -INFINITY; ps[x] = 0.f; }
+    for (int u = 0; u < ntile; ++u) {
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < kTileVec; ++v) {
+        const int f = tid + v * kScanBlock;
+        if (f < nv) *reinterpret_cast<float4*>(tile + (4 * f / M) * RS + (4 * f % M)) = rv[v];
+      }
+      __syncthreads();
+      if (u + 1 < ntile) BCJR_LOAD_TILE(q, u + 1);
+      else if (q + 1 < nstep) BCJR_LOAD_TILE(q + 1, 0);
+      const int i0 = u * R;
+      if (fwd) {
+        // out(o) += over tile rows i: vf(i) + Qn(i, o)
+        const int nout = M > kScanBlock ? M / kScanBlock : 1;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (x >= nout) break;
+          const int o = M > kScanBlock ? tid + x * kScanBlock : tid / tpo;
+          const int ch = M > kScanBlock ? 0 : tid % tpo;
+          float tm = -INFINITY;
+          for (int r = ch; r < R; r += tpo) tm = fmaxf(tm, vf[i0 + r] + tile[r * RS + o]);
+          if (tm == -INFINITY) continue;
+          float ts = 0.f;
+          for (int r = ch; r < R; r += tpo) ts += ex2(vf[i0 + r] + tile[r * RS + o] - tm);
+          lse_merge(pm[x], ps[x], tm, ts);
+        }
+      } else {
+        // out(i0 + row) = rs + m_in + LSE_j' (Qn(i, j') + vf(j')), complete within the tile
+        const int row = tid / tpr, ch = tid % tpr;
+        float tm = -INFINITY;
+        for (int j = ch; j < M; j += tpr) tm = fmaxf(tm, tile[row * RS + j] + vf[j]);
+        float ts = 0.f;
+        if (tm != -INFINITY)
+          for (int j = ch; j < M; j += tpr) ts += ex2(tile[row * RS + j] + vf[j] - tm);
+        group_lse(tm, ts, tpr);
+        if (ch == 0) vb[i0 + row] = rsd[i0 + row] + m_in + (double)tm + (double)lg2(ts);
+      }
+    }
+    if (fwd) {
+      const int nout = M > kScanBlock ? M / kScanBlock : 1;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (x >= nout) break;
+        group_lse(pm[x], ps[x], M > kScanBlock ? 1 : tpo);
+        const int o = M > kScanBlock ? tid + x * kScanBlock : tid / tpo;
+        if (M > kScanBlock || tid % tpo == 0) vb[o] = m_in + (double)pm[x] + (double)lg2(ps[x]);
+      }
+    }
+    __syncthreads();
+    double* t = va; va = vb; vb = t;
+  }
+#undef BCJR_LOAD_TILE
+}
+
+}  // namespace
+
+int launch_scan_bounds(const float* rows, const double* rscale, int64_t chains, int64_t ptot, int M,
+                       double* lam0, double* rho1, double* sc0, void* stream) {
+  if (chains <= 0) return 0;
+  if (M < 4 || M > 1024 || (M & (M - 1))) return (int)hipErrorInvalidValue;
+  const int R = M * M <= kTileFloats ? M : kTileFloats / M;
+  const size_t lds = (size_t)(3 * M + 4) * sizeof(double) + (size_t)M * sizeof(float) +
+                     (size_t)R * (M + 4) * sizeof(float);
+  hipLaunchKernelGGL(k_scan_bounds, dim3((unsigned)chains, 2), dim3(kScanBlock), lds,
+                     static_cast<hipStream_t>(stream), rows, rscale, (long long)ptot, M, R, lam0,
+                     rho1, sc0);
+  return (int)hipGetLastError();
+}
+
+}  // namespace bcjr

@@ -290,13 +290,42 @@ struct CodebookLane<C, true> {
 
 // ---------------------------------------------------------------------------------------------
 // Forward: soft codeword and log Z.
+//
+// Boundary modes (BM) for the segmented forward of long chains (parallel in L). The forward
+// and backward butterfly messages obey lam_{t+1} = lam_t (x) A_t and rho_t = A_{t+1} (x) rho_{t+1}
+// in the (log-sum-exp, +) semiring with ONE M x M matrix per step, A_t(i, j) = emission of the
+// state s with s >> k = i and s mod M = j. A segment [t0, t1) therefore has one transfer matrix
+// Q = A_{t0} ... A_{t1-1} serving both directions: lam_{t1} = lam_{t0} (x) Q and
+// rho_{t0-1} = Q (x) rho_{t1-1}.
+//   BM = 0: a whole chain, free start and end (the ordinary forward).
+//   BM = 2: transfer rows. Virtual chain v*M + i runs segment v from lam_{t0} = one-hot(i)
+//           (-kFar elsewhere) and writes its final LSE lam_{t1}(j) for all j as row i of the
+//           segment's Q: fp32 offsets from the row's integer-floor maximum, plus that row
+//           scale (N + the floor, log2, double). Phase A only; no history.
+//   BM = 1: a segment with boundary messages: lam_{t0} = lam0 + N0, rho_{t1-1} = rho1 + Np0
+//           (normalised vectors and their scales from the scan over segments), so that
+//           log2 Z = N + Np0 + LSE_j (lam_{t1}(j) - N + rho1(j)) and the posteriors are the
+//           whole chain's. Writes w_hat for the segment's steps and log Z from segment 0.
+// Virtual chain v (BM 1) or v = chain / M (BM 2) is segment jbase + v % nseg of original chain
+// v / nseg; its weights start at (v / nseg) * lfull + (jbase + v % nseg) * seglen.
 // ---------------------------------------------------------------------------------------------
-template <class C, bool CK>
+struct SegArgs {
+  long long nseg, jbase, seglen, lfull, ptot;
+  const double* lam0;  // [chains][ptot][M] normalised forward boundary messages
+  const double* rho1;  // [chains][ptot][M] normalised backward boundary messages
+  const double* sc0;   // [chains][ptot][2] their scales N0, Np0
+  float* rows;         // BM 2 output: [chains][ptot][M][M] offsets from each row's scale
+  double* rscale;      // BM 2 output: [chains][ptot][M] row scales
+};
+constexpr float kFar = 1e30f;  // stands in for -infinity without producing inf - inf
+
+template <class C, bool CK, int BM = 0>
 __global__ void __launch_bounds__(C::BLOCK)
 k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long long B, long long L,
              Consts k, float* __restrict__ w_hat, float* __restrict__ log_z,
              double* __restrict__ saved_lz, float* __restrict__ saved_what, void* __restrict__ ws,
-             size_t slot_bytes, long long units, long long seg_arg) {
+             size_t slot_bytes, long long units, long long seg_arg, SegArgs sa) {
+  static_assert(BM == 0 || !CK, "segmented modes use the full history");
   using P = typename C::P;
   using MT = typename C::MT;
   constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
@@ -327,14 +356,35 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
   for (long long unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const long long b = unit * SPB + q;
     const bool valid = b < B;
-    const float* __restrict__ wb = w + (valid ? b : B - 1) * L;
+    const long long bb = valid ? b : B - 1;
+    // segment of an original chain (BM 1, 2): its weights, and its boundary-vector index
+    const long long vch = BM == 2 ? bb / M : bb;
+    const long long sg = BM ? vch / sa.nseg * sa.ptot + sa.jbase + vch % sa.nseg : 0;
+    const long long wofs = BM ? vch / sa.nseg * sa.lfull + (sa.jbase + vch % sa.nseg) * sa.seglen
+                              : bb * L;
+    const float* __restrict__ wb = w + wofs;
 
     MT lc[G][K];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int a = 0; a < K; ++a) lc[g][a] = (MT)0;
     double N = 0.0, lz2 = 0.0;
+    if constexpr (BM == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) lc[g][a] = (MT)0;
+    } else if constexpr (BM == 1) {
+      const double* l0 = sa.lam0 + sg * M;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) lc[g][a] = (MT)l0[p + g * LPS + a * NG];
+      N = sa.sc0[sg * 2];
+    } else {
+      const long long i0 = bb % M;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) lc[g][a] = (p + g * LPS + a * NG == i0) ? (MT)0 : (MT)-kFar;
+    }
 
     // One forward step: the column offsets lc of step t -> those of step t + 1 (t < L - 1).
     auto advance = [&](long long t) {
@@ -377,8 +427,10 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 
     // ---- phase A: forward messages lam, t = 0 .. L-1 -------------------------------------
     for (long long t = 0; t < L; ++t) {
-      if (seg == 0 || t % seg == 0) store_vec<KG>(hist(seg ? t / seg : t), &lc[0][0]);
-      if (p == 0) ns[t * SPB + q] = N;
+      if constexpr (BM != 2) {
+        if (seg == 0 || t % seg == 0) store_vec<KG>(hist(seg ? t / seg : t), &lc[0][0]);
+        if (p == 0) ns[t * SPB + q] = N;
+      }
       if (t == L - 1) {
         const float u = k.sc * wb[t];
         MT out[G][K];
@@ -403,6 +455,35 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             mx = tmax(mx, out[g][r]);
           }
         }
+        if constexpr (BM == 2) {  // row i0 of the segment's transfer matrix
+          MT v1[1] = {mx};
+          chain_reduce<C, 1, 1u>(v1, red, rp);
+          const MT sh = floor(v1[0]);
+          if (valid) {
+            const long long ri = sg * M + bb % M;
+            float* row = sa.rows + ri * M;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              float o4[K];
+#pragma unroll
+              for (int r = 0; r < K; ++r) o4[r] = (float)(out[g][r] - sh);
+              store_vec<K>(row + K * (p + g * LPS), o4);
+            }
+            if (p == 0) sa.rscale[ri] = N + (double)sh;
+          }
+          break;
+        }
+        if constexpr (BM == 1) {  // the end boundary: weight by rho_{t1-1}
+          const double* r1 = sa.rho1 + sg * M;
+          mx = (MT)-INFINITY;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              out[g][r] += (MT)r1[K * (p + g * LPS) + r];
+              mx = tmax(mx, out[g][r]);
+            }
+        }
         MT v1[1] = {mx};
         chain_reduce<C, 1, 1u>(v1, red, rp);
         float s2 = 0.f;
@@ -413,9 +494,13 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         float v2[1] = {s2};
         chain_reduce<C, 1, 0u>(v2, red, rp);
         lz2 = N + ((double)v1[0] + (double)lg2(v2[0]));
+        if constexpr (BM == 1) lz2 += sa.sc0[sg * 2 + 1];
         break;
       }
       advance(t);
+    }
+    if constexpr (BM == 2) {
+      continue;  // transfer rows need no backward sweep
     }
     __syncthreads();  // phase-A history writes (incl. other lanes' N) visible to phase B
 
@@ -423,11 +508,20 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
     // Segment by segment (the whole chain is one segment with the full history); with
     // checkpoints, each segment's forward offsets are replayed from its checkpoint first.
     MT rr[G][K];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int r = 0; r < K; ++r) rr[g][r] = (MT)0;
     double Np = 0.0;
+    if constexpr (BM == 1) {
+      const double* r1 = sa.rho1 + sg * M;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) rr[g][r] = (MT)r1[K * (p + g * LPS) + r];
+      Np = sa.sc0[sg * 2 + 1];
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) rr[g][r] = (MT)0;
+    }
     const long long nseg = seg ? ncp : 1;
     for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
       const long long t0 = seg ? sgi * seg : 0;
@@ -498,8 +592,8 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         chain_reduce<C, 3, 4u>(v3, red, rp);
         if (valid && p == 0) {
           const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
-          w_hat[b * L + t] = wh;
-          saved_what[b * L + t] = wh;
+          w_hat[wofs + t] = wh;
+          if constexpr (BM == 0) saved_what[b * L + t] = wh;
         }
         if (t == 0) break;
         const MT sh = floor(v3[2]);
@@ -514,9 +608,14 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         if constexpr (C::DB) mb ^= 1; else __syncthreads();
       }
     }
-    if (valid && p == 0) {
-      log_z[b] = (float)(lz2 * (double)kLn2);
-      saved_lz[b] = lz2;
+    if constexpr (BM == 0) {
+      if (valid && p == 0) {
+        log_z[b] = (float)(lz2 * (double)kLn2);
+        saved_lz[b] = lz2;
+      }
+    } else {
+      if (valid && p == 0 && sa.jbase + vch % sa.nseg == 0)
+        log_z[vch / sa.nseg] = (float)(lz2 * (double)kLn2);
     }
   }
 }
@@ -882,10 +981,12 @@ int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   if (grid <= 0) return (int)hipErrorInvalidConfiguration;
   if (ckpt)
     hipLaunchKernelGGL((k_sparse_fwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
-                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg);
+                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg,
+                       SegArgs{});
   else
     hipLaunchKernelGGL((k_sparse_fwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
-                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg);
+                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg,
+                       SegArgs{});
   return (int)hipGetLastError();
 }
 
@@ -948,12 +1049,43 @@ int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
   return run_bwd_p<n, k, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt, st);
 }
 
+// Segmented forward launches (BM 1: segments with boundary messages, BM 2: transfer rows).
+template <int n, int k, class P, int BM>
+int run_fwd_seg_p(const float* cb, const float* w, long long Bv, long long L, float T,
+                  float* w_hat, float* log_z, void* ws, const SegArgs& sa, hipStream_t st) {
+  SparseGeom g;
+  if (!sparse_geom(n, k, Bv, fwd_kind<P>(), &g)) return (int)hipErrorInvalidValue;
+  using C = Cfg<(1 << k), geom_g(n, k, fwd_kind<P>()), geom_lps(n, k, fwd_kind<P>()), P, false>;
+  if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
+  const Consts kc = make_consts(T, P::kPrecise);
+  const size_t slot = BM == 2 ? 0 : sparse_fwd_slot_bytes(g, L, false);
+  const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_fwd<C, false, BM>),
+                                 C::BLOCK, g.slots);
+  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_sparse_fwd<C, false, BM>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb,
+                     w, Bv, L, kc, w_hat, log_z, (double*)nullptr, (float*)nullptr, ws, slot,
+                     (long long)g.units, 0LL, sa);
+  return (int)hipGetLastError();
+}
+
+template <int n, int k, int BM>
+int run_fwd_seg(const float* cb, const float* w, long long Bv, long long L, float T,
+                float* w_hat, float* log_z, void* ws, const SegArgs& sa, hipStream_t st) {
+  if constexpr (precise_fits<n, k>())
+    if (use_precise<n, k>(T))
+      return run_fwd_seg_p<n, k, Precise, BM>(cb, w, Bv, L, T, w_hat, log_z, ws, sa, st);
+  return run_fwd_seg_p<n, k, Fast, BM>(cb, w, Bv, L, T, w_hat, log_z, ws, sa, st);
+}
+
 }  // namespace
 
 // Instantiated shapes: see geom_supported().
 #define BCJR_SPARSE_SHAPES(X) \
   X(4, 2) X(5, 2) X(6, 2) X(7, 2) X(8, 2) X(9, 2) X(10, 2) X(11, 2) X(12, 2) X(13, 2) X(14, 2) \
   X(15, 2) X(16, 2)
+// Shapes with the segmented forward for long chains (its transfer matrices grow as (S/K)^2).
+#define BCJR_SCAN_SHAPES(X) \
+  X(4, 2) X(5, 2) X(6, 2) X(7, 2) X(8, 2) X(9, 2) X(10, 2) X(11, 2) X(12, 2)
 
 int launch_sparse_forward(const SparseGeom& g, const float* codebook, const float* w, int64_t B,
                           int64_t L, float T, float* w_hat, float* log_z, float* saved, void* ws,
@@ -991,6 +1123,29 @@ int launch_fill_zero(float* dst, int64_t count, void* stream) {
 bool sparse_shape_built(int n, int k) {
 #define X(N_, K_) if (n == N_ && k == K_) return true;
   BCJR_SPARSE_SHAPES(X)
+#undef X
+  return false;
+}
+
+int launch_sparse_forward_seg(int mode, int n, int k, const float* codebook, const float* w,
+                              int64_t Bv, int64_t L, float T, float* w_hat, float* log_z, void* ws,
+                              const SegLaunch& sl, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SegArgs sa{sl.nseg, sl.jbase, sl.seglen, sl.lfull, sl.ptot, sl.lam0, sl.rho1, sl.sc0,
+                   sl.rows, sl.rscale};
+#define X(N_, K_)                                                                            \
+  if (n == N_ && k == K_)                                                                    \
+    return mode == 2 ? run_fwd_seg<N_, K_, 2>(codebook, w, Bv, L, T, w_hat, log_z, ws, sa, st) \
+                     : run_fwd_seg<N_, K_, 1>(codebook, w, Bv, L, T, w_hat, log_z, ws, sa, st);
+  BCJR_SCAN_SHAPES(X)
+#undef X
+  return (int)hipErrorInvalidValue;
+}
+
+bool scan_shape_built(int n, int k) {
+#define X(N_, K_) \
+  if (n == N_ && k == K_) return true;
+  BCJR_SCAN_SHAPES(X)
 #undef X
   return false;
 }

@@ -50,6 +50,9 @@ WORKLOADS = {
                 notes="2048x2048 N(0,1) -> 16384 x 256, S=65536"),
     5: Workload(5, "dense-s256", 8, 8, 1024, 1024, (0.2,), dense=True,
                 notes="fully connected S=256, theta N(0,1) [256,256], 1024 x 1024"),
+    6: Workload(6, "long-chain-s256", 8, 2, 1, 1 << 20, (0.1,), matrix=(1024, 1024),
+                notes="a 1024x1024 N(0,1) matrix quantised as ONE chain of 2^20 steps, S=256; "
+                      "the segmented (parallel-in-L) forward"),
 }
 
 

@@ -99,6 +99,10 @@ def parse():
                     help="chains of the dense workload timed on the CPU oracle")
     ap.add_argument("--export", action="store_true",
                     help="time the hard-code export (pack / unpack of Viterbi paths) instead")
+    ap.add_argument("--seg-len", type=int, default=0,
+                    help="segment length of the segmented forward (workload 6); 0 = default")
+    ap.add_argument("--cpu-scan-steps", type=int, default=1 << 18,
+                    help="chain steps timed on the CPU oracle for workload 6")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -302,6 +306,104 @@ def bench_export(args, wl):
     }))
 
 
+# Segmented forward of long chains (parallel in L): phase 1 runs the forward (alpha) recursion
+# from S/K one-hot starts per segment (alpha side: 4.5 VALU + 1.25 trans = 7.0 slots per
+# state-step, over L * S * S/K state-steps), phase 3 the full forward over L * S state-steps
+# (16.5 slots); the boundary scan between them does O(segments * (S/K)^2) work, counted as 0.
+SCAN_PHASE1_SLOTS = 4.5 + 1.25 * TRANS_SLOTS
+
+
+def cpu_baseline_scan(wl, c, w, T, steps):
+    import oracle
+    cores = oracle.set_threads(0)
+    t0 = time.perf_counter()
+    oracle.sparse_forward(wl.n, wl.k, c, w[:, :steps], T)
+    dt = time.perf_counter() - t0
+    return {
+        "value": wl.B * steps * wl.S / dt,
+        "unit": "state-steps/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"first {steps} of {wl.L} steps of the chain (S={wl.S}), fp64 oracle forward "
+                  f"(sequential in L; one chain runs on one thread), {dt:.1f} s",
+    }
+
+
+def bench_scan(args, wl):
+    import numpy as np
+    import torch
+
+    from bcjr_soft_decoding_amd import bcjr, synth
+    T = args.temp if args.temp is not None else wl.temps[0]
+    n, k, B, L, S = wl.n, wl.k, wl.B, wl.L, wl.S
+    M = S >> k
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c_np, w_np = synth.codebook(wl.index), synth.weights(wl.index)
+    c, w = torch.from_numpy(c_np).to(dev), torch.from_numpy(w_np).to(dev)
+    seg = bcjr.bcjr_scan_segment_length(n, k, B, L, args.seg_len)
+    ws = torch.empty(bcjr.bcjr_scan_workspace_bytes(n, k, B, L, seg), dtype=torch.uint8, device=dev)
+    w_hat = torch.empty_like(w)
+    log_z = torch.empty(B, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        bcjr.bcjr_forward_scan(c, w, n, k, T, seg, w_hat, log_z, ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        bcjr.bcjr_forward_scan(c, w, n, k, T, seg, w_hat, log_z, ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    assert torch.isfinite(w_hat).all() and torch.isfinite(log_z).all()
+    # the sequential forward on the same chain, for reference (one untimed warm-up)
+    wh2, lz2, _ = bcjr.bcjr_forward(c, w, n, k, T)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    bcjr.bcjr_forward(c, w, n, k, T, wh2, lz2)
+    torch.cuda.synchronize()
+    seq_ms = (time.perf_counter() - t1) * 1e3
+    diff = float((w_hat - wh2).abs().max() / wh2.abs().max())
+    slots = SCAN_PHASE1_SLOTS * L * S * M * B + op_slots("fwd") * L * S * B
+    achieved = slots / (call_ms * 1e-3) / 1e12
+    out = {
+        "metric": "segmented BCJR forward (parallel in L) trellis state-steps/sec (1 MI355X)",
+        "value": B * L * S / (elapsed / args.steps),
+        "unit": "state-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "L": L, "S": S, "k": k, "T": T,
+                   "segment_length": seg, "segments": -(-L // seg),
+                   "workspace_bytes": int(ws.numel()), "parallelism": "single-gpu"},
+        "sequential_forward_ms": seq_ms,
+        "speedup_vs_sequential": seq_ms / (elapsed * 1e3 / args.steps),
+        "max_rel_diff_vs_sequential": diff,
+        "roofline": {
+            "bound": "alu",
+            "kernel": "bcjr_forward_scan (k_sparse_fwd transfer rows + k_scan_bounds + "
+                      "k_sparse_fwd segments)",
+            "achieved": achieved,
+            "peak": PEAK_TOPS,
+            "unit": "Tops/s",
+            "frac": achieved / PEAK_TOPS,
+            "slots_per_launch": slots,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_scan(wl, c_np, w_np, T, min(args.cpu_scan_steps, L))
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -325,6 +427,8 @@ def main():
         return bench_export(args, wl)
     if wl.dense:
         return bench_dense(args, wl)
+    if wl.index == 6:
+        return bench_scan(args, wl)
     T = args.temp if args.temp is not None else wl.temps[0]
     n, k, B, L, S = wl.n, wl.k, wl.B, wl.L, wl.S
     c_np, w_np, g_np = synth.codebook(args.workload), synth.weights(args.workload), synth.upstream_grad(args.workload)

@@ -134,6 +134,42 @@ bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, in
                            int32_t* states, float* w_hard, void* ws, size_t ws_bytes,
                            bcjr_stream_t stream);
 
+/* ---- Segmented forward for few, long chains (parallel in L) -----------------------------------
+ * The same w_hat and log_z as bcjr_forward (up to rounding), computed with parallelism along
+ * the chain. The abstract identifies the forward-backward with the transfer-matrix computation
+ * of a 1D Ising-like chain; transfer matrices compose associatively, so a chain can be cut
+ * into segments whose transfer matrices are formed independently and then combined. Here a
+ * chain is cut into segments of seg_len steps (the last one shorter if seg_len does not divide
+ * L); each segment's (S/K) x (S/K) log-semiring transfer matrix between butterfly messages is
+ * computed from S/K one-hot starts, the boundary messages are scanned over the segments in
+ * double precision, and every segment runs its forward-backward from its boundary messages.
+ * Phase 1 costs S/K times the forward recursion's work, so this pays where chains are too few
+ * to fill the device and L is long (e.g. one chain of 2^20 steps at S = 256: ~300x faster
+ * than bcjr_forward; at S = 4096 it is not faster). No backward: the result is the forward's
+ * w_hat and log Z only.
+ *
+ * seg_len  segment length in steps, > 0, or 0 for the default, about sqrt(L) steps scaled by
+ *          the boundary scan's cost per segment (which grows with (S/K)^2), at least 16;
+ *          a value >= L runs the chain as one segment
+ * Built for k = 2, n = 4..12 (BCJR_E_UNSUPPORTED otherwise). Errors as bcjr_forward, plus
+ * BCJR_E_ARG for seg_len < 0.
+ */
+/* The segment length a call with these arguments uses (0 if the arguments are invalid). */
+int64_t bcjr_scan_segment_length(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len);
+/* Workspace bytes for bcjr_forward_scan; no device needed; 0 if invalid or B == 0. Holds the
+ * transfer matrices (B x segments x (S/K)^2 doubles), the boundary messages and the segment
+ * kernels' per-slot histories. */
+size_t bcjr_scan_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len);
+/*
+ * w      DEVICE [B,L]  read only
+ * w_hat  DEVICE [B,L]  written
+ * log_z  DEVICE [B]    written
+ * ws     DEVICE, ws_bytes >= bcjr_scan_workspace_bytes(tr, B, L, seg_len), 16-byte aligned
+ */
+bcjr_status bcjr_forward_scan(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                              float T, int64_t seg_len, float* w_hat, float* log_z, void* ws,
+                              size_t ws_bytes, bcjr_stream_t stream);
+
 /* ---- Hard-code export (bitshift trellis) ------------------------------------------------------
  * The zero-temperature end of the method: the hard code that the abstract says is recovered as
  * T -> 0. A state path of the bitshift trellis is fixed by its first state and the k bits each

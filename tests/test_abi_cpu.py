@@ -242,3 +242,51 @@ def test_qat_driver_validates_before_any_gpu_call():
         qat.QATConfig(n=3, k=2).check()
     cfg = qat.QATConfig(t0=0.3, t_end=0.01, steps=5)
     assert qat.temperature(cfg, 0) == pytest.approx(0.3) and qat.temperature(cfg, 4) == pytest.approx(0.01)
+
+
+def test_scan_size_queries_and_plan(lib):
+    # default segment length ~ sqrt(L), longer for wider transfer matrices, at least 16 steps
+    d20 = bcjr.bcjr_scan_segment_length(8, 2, 1, 1 << 20)
+    d16 = bcjr.bcjr_scan_segment_length(8, 2, 1, 1 << 16)
+    assert 512 <= d20 <= 2048 and 128 <= d16 <= 512 and d16 < d20
+    assert bcjr.bcjr_scan_segment_length(12, 2, 1, 1 << 16) > 2 * d16
+    assert bcjr.bcjr_scan_segment_length(4, 2, 1, 20) == 16
+    assert bcjr.bcjr_scan_segment_length(8, 2, 4, 5000, 300) == 300    # explicit length kept
+    assert bcjr.bcjr_scan_segment_length(8, 2, 4, 5000, -1) == 0       # invalid
+    assert bcjr.bcjr_scan_segment_length(13, 2, 4, 5000) == 0          # not built for S > 4096
+    # workspace: transfer matrices B * P * M^2 doubles dominate; a single segment needs none
+    M, B, L, seg = 64, 2, 4096, 256
+    ws = bcjr.bcjr_scan_workspace_bytes(8, 2, B, L, seg)
+    assert ws >= B * (L // seg) * M * M * 8
+    one = bcjr.bcjr_scan_workspace_bytes(8, 2, B, L, L)
+    assert 0 < one < B * M * M * 8 + bcjr.bcjr_workspace_bytes(8, 2, B, L, bcjr.FWD) + 65536
+    # a ragged tail adds one segment
+    assert bcjr.bcjr_scan_workspace_bytes(8, 2, B, L + 1, seg) > ws
+    assert bcjr.bcjr_scan_workspace_bytes(8, 2, 0, L, seg) == 0
+
+
+def test_scan_rejects_bad_arguments_without_device(lib):
+    P = ctypes.c_void_p
+
+    def scan(n=8, k=2, cb=0x1000, w=0x2000, B=2, L=64, T=0.5, seg=16, wh=0x3000, lz=0x4000,
+             ws=0x6000, wsb=1 << 40):
+        tr = bcjr.Trellis(n, k, 1, cb)
+        return lib.bcjr_forward_scan(ctypes.byref(tr), P(w), B, L, T, seg, P(wh), P(lz), P(ws),
+                                     wsb, None)
+
+    assert lib.bcjr_forward_scan(None, None, 1, 1, 1.0, 0, None, None, None, 0, None) == bcjr.BCJR_E_ARG
+    assert scan(seg=-1) == bcjr.BCJR_E_ARG
+    assert scan(T=0.0) == bcjr.BCJR_E_ARG
+    assert scan(T=float("nan")) == bcjr.BCJR_E_ARG
+    assert scan(cb=0) == bcjr.BCJR_E_ARG
+    assert scan(w=0) == bcjr.BCJR_E_ARG
+    assert scan(wh=0) == bcjr.BCJR_E_ARG
+    assert scan(lz=0) == bcjr.BCJR_E_ARG
+    assert scan(n=13) == bcjr.BCJR_E_UNSUPPORTED
+    assert scan(n=0) == bcjr.BCJR_E_SHAPE
+    assert scan(L=0) == bcjr.BCJR_E_SHAPE
+    assert scan(B=-1) == bcjr.BCJR_E_SHAPE
+    need = bcjr.bcjr_scan_workspace_bytes(8, 2, 2, 64, 16)
+    assert scan(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
+    assert scan(ws=0x6008) == bcjr.BCJR_E_WORKSPACE
+    assert scan(B=0, w=0, wh=0, lz=0, ws=0, wsb=0) == bcjr.BCJR_OK

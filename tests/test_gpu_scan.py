@@ -1,0 +1,103 @@
+"""The segmented (parallel-in-L) forward for long chains against the oracle's sequential
+forward-backward and against the GPU's sequential forward."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bcjr_soft_decoding_amd import bcjr, synth
+from tests.gpu_helpers import RTOL_FWD, assert_normwise, assert_rel, dev, log_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bcjr.lib()
+
+
+CASES = [
+    (8, 1, 4096, 256, 0.3),    # segments divide L
+    (8, 3, 1000, 64, 0.1),     # ragged tail segment
+    (4, 5, 333, 16, 1.0),      # S = 16, many segments
+    (6, 2, 500, 2, 0.3),       # segments shorter than n/k: transfer rows with unreachable states
+    (8, 2, 777, 100, 0.02),    # fp64 messages
+    (12, 1, 1200, 256, 0.1),   # S = 4096 (M = 1024)
+    (10, 2, 1500, 0, 0.2),     # default segment length
+    (8, 2, 100, 1000, 0.5),    # one segment (seg >= L)
+    (5, 4, 64, 16, 0.5),       # odd n
+    (8, 2, 17, 1, 0.5),        # one step per segment
+    (11, 2, 600, 64, 0.2),     # M = 512: several LDS tiles per transfer matrix
+    (7, 3, 900, 50, 0.3),      # M = 32
+]
+
+
+@pytest.mark.parametrize("n,B,L,seg,T", CASES)
+def test_scan_matches_oracle_and_sequential(n, B, L, seg, T):
+    k = 2
+    c = synth.normal(11000 + n, (1 << n,))
+    w = synth.normal(11100 + n + L, (B, L))
+    used = bcjr.bcjr_scan_segment_length(n, k, B, L, seg)
+    log_case(f"scan n={n} B={B} L={L} seg={seg} (used {used}) T={T}")
+    wh, lz = bcjr.bcjr_forward_scan(dev(c), dev(w), n, k, T, seg)
+    wh2, lz2, _ = bcjr.bcjr_forward(dev(c), dev(w), n, k, T)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_forward(n, k, c, w, T)
+    assert_normwise(wh.cpu().numpy(), ref["w_hat"], RTOL_FWD, "w_hat vs oracle")
+    assert_rel(lz.cpu().numpy(), ref["log_z"], RTOL_FWD, "log_z vs oracle")
+    assert_normwise(wh.cpu().numpy(), wh2.cpu().numpy(), RTOL_FWD, "w_hat vs sequential")
+    assert_rel(lz.cpu().numpy(), lz2.cpu().numpy(), RTOL_FWD, "log_z vs sequential")
+
+
+def test_scan_zero_chains_is_a_no_op():
+    c = dev(synth.normal(11200, (256,)))
+    w = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    log_case("scan B=0")
+    wh, lz = bcjr.bcjr_forward_scan(c, w, 8, 2, 0.5, 16)
+    torch.cuda.synchronize()
+    assert wh.numel() == 0 and lz.numel() == 0
+
+
+def test_scan_deterministic():
+    n, k, B, L, T = 8, 2, 2, 3000, 0.2
+    c = dev(synth.normal(11300, (1 << n,)))
+    w = dev(synth.normal(11301, (B, L)))
+    log_case("scan determinism")
+    a = bcjr.bcjr_forward_scan(c, w, n, k, T, 100)
+    b = bcjr.bcjr_forward_scan(c, w, n, k, T, 100)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_scan_long_chain_against_oracle():
+    """One 2^18-step chain at S = 256 with the default segment length (the benchmark's launch
+    configuration at a quarter of its length)."""
+    n, k, L, T = 8, 2, 1 << 18, 0.1
+    c = synth.normal(11400, (1 << n,))
+    w = synth.normal(11401, (1, L))
+    log_case(f"scan long chain n={n} L={L} seg={bcjr.bcjr_scan_segment_length(n, k, 1, L)}")
+    wh, lz = bcjr.bcjr_forward_scan(dev(c), dev(w), n, k, T)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_forward(n, k, c, w, T)
+    assert_normwise(wh.cpu().numpy(), ref["w_hat"], RTOL_FWD, "w_hat")
+    assert_rel(lz.cpu().numpy(), ref["log_z"], RTOL_FWD, "log_z")
+
+
+def test_scan_full_workload_in_bench_configuration():
+    """Workload 6 (one chain of 2^20 steps, S = 256) with the default segment length, as
+    bench.py runs it: the whole chain against the oracle and the sequential GPU forward."""
+    i = 6
+    wl = synth.WORKLOADS[i]
+    c, w = synth.codebook(i), synth.weights(i)
+    T = wl.temps[0]
+    log_case(f"scan full workload {i} ({wl.name}) L={wl.L} "
+             f"seg={bcjr.bcjr_scan_segment_length(wl.n, wl.k, wl.B, wl.L)}")
+    wh, lz = bcjr.bcjr_forward_scan(dev(c), dev(w), wl.n, wl.k, T)
+    wh2, lz2, _ = bcjr.bcjr_forward(dev(c), dev(w), wl.n, wl.k, T)
+    torch.cuda.synchronize()
+    assert_normwise(wh.cpu().numpy(), wh2.cpu().numpy(), RTOL_FWD, "w_hat vs sequential")
+    assert_rel(lz.cpu().numpy(), lz2.cpu().numpy(), RTOL_FWD, "log_z vs sequential")
+    ref = oracle.sparse_forward(wl.n, wl.k, c, w, T)
+    assert_normwise(wh.cpu().numpy(), ref["w_hat"], RTOL_FWD, "w_hat vs oracle")
+    assert_rel(lz.cpu().numpy(), ref["log_z"], RTOL_FWD, "log_z vs oracle")
