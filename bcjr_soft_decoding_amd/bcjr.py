@@ -24,6 +24,7 @@ EXPORTED = (
     "bcjr_dense_workspace_bytes", "bcjr_dense_forward", "bcjr_dense_backward",
     "bcjr_code_words", "bcjr_pack_code", "bcjr_unpack_code", "bcjr_status_string",
     "bcjr_scan_segment_length", "bcjr_scan_workspace_bytes", "bcjr_forward_scan",
+    "bcjr_scan_backward_workspace_bytes", "bcjr_backward_scan",
 )
 
 
@@ -90,6 +91,10 @@ def lib() -> ctypes.CDLL:
     L.bcjr_scan_workspace_bytes.restype = SZ
     L.bcjr_forward_scan.argtypes = [TP, P, I64, I64, F, I64, P, P, P, SZ, P]
     L.bcjr_forward_scan.restype = ctypes.c_int
+    L.bcjr_scan_backward_workspace_bytes.argtypes = [TP, I64, I64, I64]
+    L.bcjr_scan_backward_workspace_bytes.restype = SZ
+    L.bcjr_backward_scan.argtypes = [TP, P, I64, I64, F, I64, P, P, P, P, P, P, SZ, P]
+    L.bcjr_backward_scan.restype = ctypes.c_int
     L.bcjr_status_string.argtypes = [ctypes.c_int]
     L.bcjr_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -187,6 +192,30 @@ def bcjr_forward_scan(codebook, w, n, k, T, seg_len=0, w_hat=None, log_z=None, w
                                  _ptr(w_hat), _ptr(log_z), _ptr(ws), ws.numel(), _stream())
     _check(st, "bcjr_forward_scan")
     return w_hat, log_z
+
+
+def bcjr_scan_backward_workspace_bytes(n: int, k: int, B: int, L: int, seg_len: int = 0) -> int:
+    tr = trellis(n, k)
+    return int(lib().bcjr_scan_backward_workspace_bytes(ctypes.byref(tr), B, L, seg_len))
+
+
+def bcjr_backward_scan(codebook, w, n, k, T, w_hat, grad_w_hat, grad_log_z=None, seg_len=0,
+                       grad_w=None, grad_codebook=None, ws=None):
+    """Segmented (parallel-in-L) backward; returns (grad_w, grad_codebook)."""
+    _f32(codebook, "codebook"); _f32(w, "w"); _f32(w_hat, "w_hat"); _f32(grad_w_hat, "grad_w_hat")
+    B, L = w.shape
+    dev = w.device
+    grad_w = torch.empty_like(w) if grad_w is None else grad_w
+    grad_codebook = torch.empty_like(codebook) if grad_codebook is None else grad_codebook
+    if ws is None:
+        nb = bcjr_scan_backward_workspace_bytes(n, k, B, L, seg_len)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    tr = trellis(n, k, codebook)
+    st = lib().bcjr_backward_scan(ctypes.byref(tr), _ptr(w), B, L, float(T), int(seg_len),
+                                  _ptr(w_hat), _ptr(grad_w_hat), _ptr(grad_log_z), _ptr(grad_w),
+                                  _ptr(grad_codebook), _ptr(ws), ws.numel(), _stream())
+    _check(st, "bcjr_backward_scan")
+    return grad_w, grad_codebook
 
 
 def bcjr_backward(codebook, w, n, k, T, saved, grad_w_hat, grad_log_z=None, grad_w=None,

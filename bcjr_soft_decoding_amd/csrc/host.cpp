@@ -149,9 +149,102 @@ bcjr_status scan_setup(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg
   return BCJR_OK;
 }
 
+// Backward plan; the partial slots cover both message precisions' geometries of both launches.
+bcjr_status scan_setup_bwd(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len,
+                           ScanPlan* plan) {
+  ScanPlan f;
+  bcjr_status st = scan_setup(tr, B, L, seg_len, &f);
+  if (st != BCJR_OK) return st;
+  const int n = tr->state_bits, k = tr->bits_per_step;
+  SparseGeom gm, gt, pm, pt;
+  if (!sparse_geom(n, k, B * f.pmain, kBwd, &gm) || !sparse_geom(n, k, B, kBwd, &gt) ||
+      !sparse_geom(n, k, B * f.pmain, kBwdP, &pm) || !sparse_geom(n, k, B, kBwdP, &pt))
+    return BCJR_E_UNSUPPORTED;
+  const int64_t slots = (gm.slots > pm.slots ? gm.slots : pm.slots) +
+                        (gt.slots > pt.slots ? gt.slots : pt.slots);
+  scan_plan_bwd(gm, gt, slots, n, k, B, L, f.seg, plan);
+  return BCJR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t bcjr_scan_backward_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L,
+                                          int64_t seg_len) {
+  ScanPlan plan;
+  if (scan_setup_bwd(tr, B, L, seg_len, &plan) != BCJR_OK || B == 0) return 0;
+  return plan.bytes;
+}
+
+bcjr_status bcjr_backward_scan(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                               float T, int64_t seg_len, const float* w_hat,
+                               const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                               float* grad_codebook, void* ws, size_t ws_bytes,
+                               bcjr_stream_t stream) {
+  ScanPlan plan;
+  bcjr_status st = scan_setup_bwd(tr, B, L, seg_len, &plan);
+  if (st != BCJR_OK) return st;
+  if (!temp_ok(T)) return BCJR_E_ARG;
+  if (grad_codebook == nullptr || tr->codebook == nullptr) return BCJR_E_ARG;
+  if (B == 0)
+    return from_hip(launch_fill_zero(grad_codebook, (int64_t)1 << tr->state_bits, stream));
+  if (!w || !w_hat || !grad_w_hat || !grad_w) return BCJR_E_ARG;
+  if (!ws_ok(ws, ws_bytes, plan.bytes)) return BCJR_E_WORKSPACE;
+  const int n = tr->state_bits, k = tr->bits_per_step;
+  const int M = (1 << n) >> k, S = 1 << n;
+  char* base = static_cast<char*>(ws);
+  SegLaunch sl{plan.pmain, 0, plan.seg, L, plan.ptot,
+               reinterpret_cast<const double*>(base + plan.lam0),
+               reinterpret_cast<const double*>(base + plan.rho1),
+               reinterpret_cast<const double*>(base + plan.sc0),
+               reinterpret_cast<float*>(base + plan.rows),
+               reinterpret_cast<double*>(base + plan.rscale),
+               reinterpret_cast<const float*>(base + plan.phi0),
+               reinterpret_cast<const float*>(base + plan.psi1),
+               reinterpret_cast<float*>(base + plan.frows)};
+  float* partial = reinterpret_cast<float*>(base + plan.partial);
+  void* slots = base + plan.slots;
+  int e = 0, g1 = 0, g2 = 0;
+  // phase 1: transfer and moment rows of every segment
+  if (plan.ptot > 1) {
+    e = launch_sparse_backward_seg(2, n, k, tr->codebook, w, B * plan.pmain * M, plan.seg, T,
+                                   w_hat, grad_w_hat, grad_log_z, grad_w, partial, slots, sl, &g1,
+                                   stream);
+    if (e == 0 && plan.tail > 0) {
+      SegLaunch st2 = sl;
+      st2.nseg = 1;
+      st2.jbase = plan.pmain;
+      e = launch_sparse_backward_seg(2, n, k, tr->codebook, w, B * M, plan.tail, T, w_hat,
+                                     grad_w_hat, grad_log_z, grad_w, partial, slots, st2, &g2,
+                                     stream);
+    }
+  }
+  // phase 2: messages and conditional expectations at every segment boundary
+  if (e == 0)
+    e = launch_scan_bounds(sl.rows, sl.rscale, sl.frows, B, plan.ptot, M,
+                           reinterpret_cast<double*>(base + plan.lam0),
+                           reinterpret_cast<double*>(base + plan.rho1),
+                           reinterpret_cast<double*>(base + plan.sc0),
+                           reinterpret_cast<float*>(base + plan.phi0),
+                           reinterpret_cast<float*>(base + plan.psi1), stream);
+  // phase 3: every segment's gradient from its boundary values, then the codebook partials
+  g1 = g2 = 0;
+  if (e == 0)
+    e = launch_sparse_backward_seg(1, n, k, tr->codebook, w, B * plan.pmain, plan.seg, T, w_hat,
+                                   grad_w_hat, grad_log_z, grad_w, partial, slots, sl, &g1,
+                                   stream);
+  if (e == 0 && plan.tail > 0) {
+    SegLaunch st2 = sl;
+    st2.nseg = 1;
+    st2.jbase = plan.pmain;
+    e = launch_sparse_backward_seg(1, n, k, tr->codebook, w, B, plan.tail, T, w_hat, grad_w_hat,
+                                   grad_log_z, grad_w, partial + (size_t)g1 * S, slots, st2, &g2,
+                                   stream);
+  }
+  if (e == 0) e = launch_reduce_slots(partial, g1 + g2, S, grad_codebook, stream);
+  return from_hip(e);
+}
 
 int64_t bcjr_scan_segment_length(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg_len) {
   ScanPlan plan;
@@ -198,7 +291,9 @@ bcjr_status bcjr_forward_scan(const bcjr_trellis* tr, const float* w, int64_t B,
     }
   }
   // phase 2: boundary messages by a scan over the segments
-  if (e == 0) e = launch_scan_bounds(rows, rscale, B, plan.ptot, M, lam0, rho1, sc0, stream);
+  if (e == 0)
+    e = launch_scan_bounds(rows, rscale, nullptr, B, plan.ptot, M, lam0, rho1, sc0, nullptr,
+                           nullptr, stream);
   // phase 3: every segment's forward-backward from its boundary messages
   if (e == 0) {
     SegLaunch sl{plan.pmain, 0, plan.seg, L, plan.ptot, lam0, rho1, sc0, nullptr, nullptr};

@@ -104,15 +104,29 @@ struct SegLaunch {
   const double* sc0;
   float* rows;
   double* rscale;
+  const float* phi0 = nullptr;  // backward only
+  const float* psi1 = nullptr;
+  float* frows = nullptr;
 };
 // mode 2: transfer rows (Bv = chains * segments * M virtual chains); mode 1: segments with
 // boundary messages (Bv = chains * segments).
 int launch_sparse_forward_seg(int mode, int n, int k, const float* codebook, const float* w,
                               int64_t Bv, int64_t L, float T, float* w_hat, float* log_z, void* ws,
                               const SegLaunch& sl, void* stream);
+// Backward counterparts: mode 2 writes transfer rows and moment rows, mode 1 runs the segments
+// and writes the codebook-gradient partials of *grid_used slots at `partial` (not reduced).
+int launch_sparse_backward_seg(int mode, int n, int k, const float* codebook, const float* w,
+                               int64_t Bv, int64_t L, float T, const float* w_hat,
+                               const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                               float* partial, void* ws, const SegLaunch& sl, int* grid_used,
+                               void* stream);
+// out[s] = sum over slots of partial[slot][s], slots in order.
+int launch_reduce_slots(const float* partial, int64_t slots, int S, float* out, void* stream);
 bool scan_shape_built(int n, int k);
-int launch_scan_bounds(const float* rows, const double* rscale, int64_t chains, int64_t ptot, int M,
-                       double* lam0, double* rho1, double* sc0, void* stream);
+// Boundary scan; with frows (moment rows) also the conditional expectations phi0 / psi1.
+int launch_scan_bounds(const float* rows, const double* rscale, const float* frows, int64_t chains,
+                       int64_t ptot, int M, double* lam0, double* rho1, double* sc0, float* phi0,
+                       float* psi1, void* stream);
 
 constexpr int64_t kScanMinSeg = 16;
 
@@ -147,6 +161,8 @@ inline int64_t scan_default_seg(int n, int k, int64_t B, int64_t L) {
 struct ScanPlan {
   int64_t seg, pmain, tail, ptot;
   size_t rows, rscale, lam0, rho1, sc0, slots, bytes;  // workspace offsets and total
+  // backward only: moment rows, Phi / Psi boundaries, codebook-gradient partials
+  size_t frows = 0, phi0 = 0, psi1 = 0, partial = 0;
 };
 
 inline void scan_plan(const SparseGeom& gmain, const SparseGeom& gtail, int n, int k, int64_t B,
@@ -166,6 +182,37 @@ inline void scan_plan(const SparseGeom& gmain, const SparseGeom& gtail, int n, i
   size_t a = sparse_fwd_ws_bytes(gmain, p->seg, false);
   if (p->tail > 0) {
     const size_t b = sparse_fwd_ws_bytes(gtail, p->tail, false);
+    if (b > a) a = b;
+  }
+  p->bytes = p->slots + round256(a);
+}
+
+// Backward plan: transfer and moment rows, the four boundary vectors and their scales, the
+// codebook-gradient partials of both segment launches (up to `partial_slots` slots), then the
+// segment kernels' per-slot histories. gmain / gtail are fp32-message backward geometries.
+inline void scan_plan_bwd(const SparseGeom& gmain, const SparseGeom& gtail, int64_t partial_slots,
+                          int n, int k, int64_t B, int64_t L, int64_t seg, ScanPlan* p) {
+  const int64_t M = ((int64_t)1 << n) >> k;
+  const int64_t S = (int64_t)1 << n;
+  p->seg = seg < L ? seg : L;
+  p->pmain = L / p->seg;
+  p->tail = L - p->pmain * p->seg;
+  p->ptot = p->pmain + (p->tail > 0 ? 1 : 0);
+  const size_t cp = (size_t)B * (size_t)p->ptot;
+  const size_t mm = p->ptot > 1 ? round256(cp * (size_t)M * (size_t)M * sizeof(float)) : 0;
+  p->rows = 0;
+  p->frows = mm;
+  p->rscale = 2 * mm;
+  p->lam0 = p->rscale + (p->ptot > 1 ? round256(cp * (size_t)M * sizeof(double)) : 0);
+  p->rho1 = p->lam0 + round256(cp * (size_t)M * sizeof(double));
+  p->sc0 = p->rho1 + round256(cp * (size_t)M * sizeof(double));
+  p->phi0 = p->sc0 + round256(cp * 2 * sizeof(double));
+  p->psi1 = p->phi0 + round256(cp * (size_t)M * sizeof(float));
+  p->partial = p->psi1 + round256(cp * (size_t)M * sizeof(float));
+  p->slots = p->partial + round256((size_t)partial_slots * (size_t)S * sizeof(float));
+  size_t a = sparse_bwd_ws_bytes(gmain, p->seg, false);
+  if (p->tail > 0) {
+    const size_t b = sparse_bwd_ws_bytes(gtail, p->tail, false);
     if (b > a) a = b;
   }
   p->bytes = p->slots + round256(a);

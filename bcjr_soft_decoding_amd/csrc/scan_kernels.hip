@@ -10,6 +10,12 @@
 // direction, sequentially over the segments, and stores every boundary vector normalised by
 // the integer floor of its maximum together with that scale, the form the segment kernels take.
 //
+// With moments (the backward's scan), the conditional expectations travel with the messages:
+//   Phi at the start of segment j+1 (j') = sum_i w(i, j') (Phi at the start of j (i) + F_j(i, j')),
+//   Psi at the end of segment j-1 (i)    = sum_j' v(i, j') (F_j(i, j') + Psi at the end of j (j')),
+// w and v being the softmax weights of the corresponding log-sum-exp, F_j the segment's moment
+// rows (k_sparse_bwd's transfer-row mode), Phi = 0 at the start and Psi = 0 at the end.
+//
 // Q_j arrives as fp32 row offsets Qn(i, .) <= 0 plus a double row scale rs(i):
 // Q(i, j) = rs(i) + Qn(i, j) (log2). Vectors and scales are double; each log-sum-exp is formed
 // against its own maximum with fp32 exponentials, so only offsets below the maximum are
@@ -43,58 +49,77 @@ __device__ double block_max(double v, double* red) {
   return r;
 }
 
-// Running log-sum-exp (max m, sum s relative to m) merged with another.
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+// Running log-sum-exp (max m, sum s relative to m, and the weighted moment sum t) merged with
+// another.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float& t, float m2, float s2,
+                                          float t2) {
   const float mn = fmaxf(m, m2);
   if (mn == -INFINITY) return;
-  s = s * ex2(m - mn) + s2 * ex2(m2 - mn);
+  const float a = ex2(m - mn), b = ex2(m2 - mn);
+  s = s * a + s2 * b;
+  t = t * a + t2 * b;
   m = mn;
 }
 
-// Combine the partial (m, s) of the `width` adjacent lanes that share an output.
-__device__ __forceinline__ void group_lse(float& m, float& s, int width) {
+// Combine the partial (m, s, t) of the `width` adjacent lanes that share an output.
+__device__ __forceinline__ void group_lse(float& m, float& s, float& t, int width) {
   for (int o = 1; o < width; o <<= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-    lse_merge(m, s, m2, s2);
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o), t2 = __shfl_xor(t, o);
+    lse_merge(m, s, t, m2, s2, t2);
   }
 }
 
 // rows: [chains][ptot][M][M] fp32 offsets; rscale: [chains][ptot][M];
 // lam0, rho1: [chains][ptot][M]; sc0: [chains][ptot][2]. R rows per tile, R * M <= kTileFloats.
+// MOM: also frows [chains][ptot][M][M] (moment rows) -> phi0, psi1 [chains][ptot][M].
+template <bool MOM>
 __global__ void __launch_bounds__(kScanBlock)
-k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale, long long ptot,
-              int M, int R, double* __restrict__ lam0, double* __restrict__ rho1,
-              double* __restrict__ sc0) {
+k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale,
+              const float* __restrict__ frows, long long ptot, int M, int R,
+              double* __restrict__ lam0, double* __restrict__ rho1, double* __restrict__ sc0,
+              float* __restrict__ phi0, float* __restrict__ psi1) {
   extern __shared__ __attribute__((aligned(16))) double smd[];
   const int RS = M + 4;  // padded tile row stride (keeps 16-byte alignment)
   double* va = smd;                                  // current boundary vector [M]
-  double* vb = va + M;                               // next one [M]
-  double* rsd = vb + M;                              // row scales of the segment [M]
-  double* red = rsd + M;                             // reduction scratch [4]
+  double* vb = va + M;                               // next one [M]; first the row scales
+  double* red = vb + M;                              // reduction scratch [4]
   float* vf = reinterpret_cast<float*>(red + 4);     // fp32 relative vector [M]
-  float* tile = vf + M;                              // [R][RS]
+  float* ma = vf + M;                                // current moment vector [M] (MOM)
+  float* mbv = ma + M;                               // next one [M] (MOM)
+  float* tile = mbv + M;                             // [R][RS]
+  float* ftile = tile + R * RS;                      // [R][RS] (MOM)
   const long long c = blockIdx.x;
   const bool fwd = blockIdx.y == 0;
   const int tid = threadIdx.x;
   const int ntile = M / R;
   const long long nstep = ptot - 1;  // matrix-vector steps of the scan
-  for (int i = tid; i < M; i += kScanBlock) va[i] = 0.0;
+  for (int i = tid; i < M; i += kScanBlock) {
+    va[i] = 0.0;
+    if (MOM) ma[i] = 0.f;
+  }
 
   // segment of scan step q: forward Q_q, backward Q_{ptot-1-q}
   auto seg_of = [&](long long q) { return c * ptot + (fwd ? q : ptot - 1 - q); };
   const int nv = R * M / 4;  // float4 vectors per tile
   // Prefetch registers: tile u of scan step q (lanes past the tile reload its first vector) and,
   // with tile 0, the thread's share of the segment's row scales (rows tid + 256 x).
-  float4 rv[kTileVec];
+  float4 rv[kTileVec], fv[MOM ? kTileVec : 1];
   double rr[4];
 #define BCJR_LOAD_TILE(Q_, U_)                                                              \
   do {                                                                                      \
     const long long sg_ = seg_of(Q_);                                                       \
-    const float4* src_ =                                                                    \
-        reinterpret_cast<const float4*>(rows + (sg_ * M + (long long)(U_) * R) * M);        \
+    const long long o_ = (sg_ * M + (long long)(U_) * R) * M;                               \
+    const float4* src_ = reinterpret_cast<const float4*>(rows + o_);                        \
     _Pragma("unroll") for (int v_ = 0; v_ < kTileVec; ++v_) {                               \
       const int f_ = tid + v_ * kScanBlock;                                                 \
       rv[v_] = src_[f_ < nv ? f_ : 0];                                                      \
+    }                                                                                       \
+    if constexpr (MOM) {                                                                    \
+      const float4* fs_ = reinterpret_cast<const float4*>(frows + o_);                      \
+      _Pragma("unroll") for (int v_ = 0; v_ < kTileVec; ++v_) {                             \
+        const int f_ = tid + v_ * kScanBlock;                                               \
+        fv[v_] = fs_[f_ < nv ? f_ : 0];                                                     \
+      }                                                                                     \
     }                                                                                       \
     if ((U_) == 0) {                                                                        \
       _Pragma("unroll") for (int x_ = 0; x_ < 4; ++x_) {                                    \
@@ -117,15 +142,24 @@ k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale,
 #pragma unroll
   for (int v = 0; v < kTileVec; ++v) rv[v] = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+  for (int v = 0; v < (MOM ? kTileVec : 1); ++v) fv[v] = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
   for (int x = 0; x < 4; ++x) rr[x] = 0.0;
   if (nstep > 0) BCJR_LOAD_TILE(0, 0);
   for (long long q = 0;; ++q) {
     const long long sgb = c * ptot + (fwd ? q : ptot - 1 - q);  // boundary this vector belongs to
     __syncthreads();
     store_normalised(va, sgb, fwd ? lam0 : rho1, sc0 + sgb * 2 + (fwd ? 0 : 1));
+    if constexpr (MOM) {
+      float* mo = (fwd ? phi0 : psi1) + sgb * M;
+      for (int i = tid; i < M; i += kScanBlock) mo[i] = ma[i];
+    }
     if (q == nstep) break;
 
-    // row scales of this step's segment, and the fp32 relative input vector
+    // row scales of this step's segment (in the output buffer: the forward consumes them
+    // before any output is written, the backward reads row i's just before writing row i),
+    // and the fp32 relative input vector
+    double* rsd = vb;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
       if (tid + x * kScanBlock < M) rsd[tid + x * kScanBlock] = rr[x];
@@ -136,15 +170,19 @@ k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale,
     for (int i = tid; i < M; i += kScanBlock)
       vf[i] = (float)((fwd ? va[i] + rsd[i] : va[i]) - m_in);
 
-    float pm[4], ps[4];  // forward partials for up to 4 outputs (M <= 1024)
+    float pm[4], ps[4], pt[4];  // forward partials for up to 4 outputs (M <= 1024)
 #pragma unroll
-    for (int x = 0; x < 4; ++x) { pm[x] = -INFINITY; ps[x] = 0.f; }
+    for (int x = 0; x < 4; ++x) { pm[x] = -INFINITY; ps[x] = 0.f; pt[x] = 0.f; }
     for (int u = 0; u < ntile; ++u) {
       __syncthreads();
 #pragma unroll
       for (int v = 0; v < kTileVec; ++v) {
         const int f = tid + v * kScanBlock;
-        if (f < nv) *reinterpret_cast<float4*>(tile + (4 * f / M) * RS + (4 * f % M)) = rv[v];
+        if (f < nv) {
+          const int e = (4 * f / M) * RS + (4 * f % M);
+          *reinterpret_cast<float4*>(tile + e) = rv[v];
+          if constexpr (MOM) *reinterpret_cast<float4*>(ftile + e) = fv[v];
+        }
       }
       __syncthreads();
       if (u + 1 < ntile) BCJR_LOAD_TILE(q, u + 1);
@@ -161,20 +199,31 @@ k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale,
           float tm = -INFINITY;
           for (int r = ch; r < R; r += tpo) tm = fmaxf(tm, vf[i0 + r] + tile[r * RS + o]);
           if (tm == -INFINITY) continue;
-          float ts = 0.f;
-          for (int r = ch; r < R; r += tpo) ts += ex2(vf[i0 + r] + tile[r * RS + o] - tm);
-          lse_merge(pm[x], ps[x], tm, ts);
+          float ts = 0.f, tt = 0.f;
+          for (int r = ch; r < R; r += tpo) {
+            const float e = ex2(vf[i0 + r] + tile[r * RS + o] - tm);
+            ts += e;
+            if constexpr (MOM) tt = __builtin_fmaf(e, ma[i0 + r] + ftile[r * RS + o], tt);
+          }
+          lse_merge(pm[x], ps[x], pt[x], tm, ts, tt);
         }
       } else {
         // out(i0 + row) = rs + m_in + LSE_j' (Qn(i, j') + vf(j')), complete within the tile
         const int row = tid / tpr, ch = tid % tpr;
         float tm = -INFINITY;
         for (int j = ch; j < M; j += tpr) tm = fmaxf(tm, tile[row * RS + j] + vf[j]);
-        float ts = 0.f;
+        float ts = 0.f, tt = 0.f;
         if (tm != -INFINITY)
-          for (int j = ch; j < M; j += tpr) ts += ex2(tile[row * RS + j] + vf[j] - tm);
-        group_lse(tm, ts, tpr);
-        if (ch == 0) vb[i0 + row] = rsd[i0 + row] + m_in + (double)tm + (double)lg2(ts);
+          for (int j = ch; j < M; j += tpr) {
+            const float e = ex2(tile[row * RS + j] + vf[j] - tm);
+            ts += e;
+            if constexpr (MOM) tt = __builtin_fmaf(e, ftile[row * RS + j] + ma[j], tt);
+          }
+        group_lse(tm, ts, tt, tpr);
+        if (ch == 0) {
+          vb[i0 + row] = rsd[i0 + row] + m_in + (double)tm + (double)lg2(ts);
+          if constexpr (MOM) mbv[i0 + row] = tt / ts;
+        }
       }
     }
     if (fwd) {
@@ -182,29 +231,44 @@ k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale,
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         if (x >= nout) break;
-        group_lse(pm[x], ps[x], M > kScanBlock ? 1 : tpo);
+        group_lse(pm[x], ps[x], pt[x], M > kScanBlock ? 1 : tpo);
         const int o = M > kScanBlock ? tid + x * kScanBlock : tid / tpo;
-        if (M > kScanBlock || tid % tpo == 0) vb[o] = m_in + (double)pm[x] + (double)lg2(ps[x]);
+        if (M > kScanBlock || tid % tpo == 0) {
+          vb[o] = m_in + (double)pm[x] + (double)lg2(ps[x]);
+          if constexpr (MOM) mbv[o] = pt[x] / ps[x];
+        }
       }
     }
     __syncthreads();
     double* t = va; va = vb; vb = t;
+    if constexpr (MOM) {
+      float* tf = ma; ma = mbv; mbv = tf;
+    }
   }
 #undef BCJR_LOAD_TILE
 }
 
 }  // namespace
 
-int launch_scan_bounds(const float* rows, const double* rscale, int64_t chains, int64_t ptot, int M,
-                       double* lam0, double* rho1, double* sc0, void* stream) {
+int launch_scan_bounds(const float* rows, const double* rscale, const float* frows, int64_t chains,
+                       int64_t ptot, int M, double* lam0, double* rho1, double* sc0, float* phi0,
+                       float* psi1, void* stream) {
   if (chains <= 0) return 0;
   if (M < 4 || M > 1024 || (M & (M - 1))) return (int)hipErrorInvalidValue;
-  const int R = M * M <= kTileFloats ? M : kTileFloats / M;
-  const size_t lds = (size_t)(3 * M + 4) * sizeof(double) + (size_t)M * sizeof(float) +
-                     (size_t)R * (M + 4) * sizeof(float);
-  hipLaunchKernelGGL(k_scan_bounds, dim3((unsigned)chains, 2), dim3(kScanBlock), lds,
-                     static_cast<hipStream_t>(stream), rows, rscale, (long long)ptot, M, R, lam0,
-                     rho1, sc0);
+  const bool mom = frows != nullptr;
+  // rows per staged tile: R * M <= 8192 floats (4096 with the moment tile beside it), so the
+  // LDS stays under 64 KiB up to M = 1024; R >= 4 keeps a backward row within one wave
+  const int tf = mom ? kTileFloats / 2 : kTileFloats;
+  const int R = M * M <= tf ? M : tf / M;
+  const size_t lds = (size_t)(2 * M + 4) * sizeof(double) + (size_t)3 * M * sizeof(float) +
+                     (size_t)(mom ? 2 : 1) * R * (M + 4) * sizeof(float);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mom)
+    hipLaunchKernelGGL(k_scan_bounds<true>, dim3((unsigned)chains, 2), dim3(kScanBlock), lds, st,
+                       rows, rscale, frows, (long long)ptot, M, R, lam0, rho1, sc0, phi0, psi1);
+  else
+    hipLaunchKernelGGL(k_scan_bounds<false>, dim3((unsigned)chains, 2), dim3(kScanBlock), lds, st,
+                       rows, rscale, frows, (long long)ptot, M, R, lam0, rho1, sc0, phi0, psi1);
   return (int)hipGetLastError();
 }
 

@@ -316,6 +316,11 @@ struct SegArgs {
   const double* sc0;   // [chains][ptot][2] their scales N0, Np0
   float* rows;         // BM 2 output: [chains][ptot][M][M] offsets from each row's scale
   double* rscale;      // BM 2 output: [chains][ptot][M] row scales
+  // backward only: the conditional expectations Phi at segment starts and Psi at segment ends
+  // ([chains][ptot][M], fp32), and (BM 2) the segment moment rows F [chains][ptot][M][M]
+  const float* phi0;
+  const float* psi1;
+  float* frows;
 };
 constexpr float kFar = 1e30f;  // stands in for -infinity without producing inf - inf
 
@@ -635,13 +640,24 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 //   dF/dw_t  = (2/T) (sum_s c(s) E_t(s) - h w_t)
 //   dF/dc(s) = sum_t [ g_t gamma_t(s) + (2/T)(w_t - c(s)) E_t(s) ].
 // ---------------------------------------------------------------------------------------------
-template <class C, bool CK>
+//
+// Boundary modes as in k_sparse_fwd. The conditional expectations compose over a segment
+// [t0, t1) through its moment matrix F(i, j) = E[sum_{t0 <= u < t1} g_u (c(s_u) - w_hat_u) |
+// butterfly i at t0, butterfly j at t1]: the forward one at t1 is a softmax-weighted average
+// over i of Phi_{t0}(i) + F(i, j), the backward one at t0 - 1 one over j of F(i, j) + Psi(j).
+//   BM = 2: virtual chain v*M + i runs segment v's lam and Phi recursions from lam = one-hot(i),
+//           Phi = 0, and writes row i of Q (as k_sparse_fwd) and of F. Phase A only.
+//   BM = 1: a segment from its boundary values lam0 + N0, Phi0 at t0 and rho1 + Np0, Psi1 at
+//           t1 - 1; log2 Z is the segment's own (as in k_sparse_fwd's mode 1), grad_w is written
+//           at the segment's steps and the codebook-gradient partials cover all its segments.
+template <class C, bool CK, int BM = 0>
 __global__ void __launch_bounds__(C::BLOCK)
 k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long long B, long long L,
              Consts k, const double* __restrict__ saved_lz, const float* __restrict__ saved_what,
              const float* __restrict__ gup, const float* __restrict__ hup,
              float* __restrict__ grad_w, float* __restrict__ partial, void* __restrict__ ws,
-             size_t slot_bytes, long long units, long long seg_arg) {
+             size_t slot_bytes, long long units, long long seg_arg, SegArgs sa) {
+  static_assert(BM == 0 || !CK, "segmented modes use the full history");
   using P = typename C::P;
   using MT = typename C::MT;
   constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
@@ -682,19 +698,46 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
     const long long b = unit * SPB + q;
     const bool valid = b < B;
     const long long bb = valid ? b : B - 1;
-    const float* __restrict__ wb = w + bb * L;
-    const float* __restrict__ gb = gup + bb * L;
-    const float* __restrict__ whb = saved_what + bb * L;
-    const float h = (hup != nullptr && valid) ? hup[bb] : 0.f;
-    const double lz2 = saved_lz[bb];
+    // segment of an original chain (BM 1, 2), as in k_sparse_fwd
+    const long long vch = BM == 2 ? bb / M : bb;
+    const long long chain = BM ? vch / sa.nseg : bb;
+    const long long sg = BM ? chain * sa.ptot + sa.jbase + vch % sa.nseg : 0;
+    const long long wofs = BM ? chain * sa.lfull + (sa.jbase + vch % sa.nseg) * sa.seglen : bb * L;
+    const float* __restrict__ wb = w + wofs;
+    const float* __restrict__ gb = gup + wofs;
+    const float* __restrict__ whb = saved_what + wofs;
+    const float h = (BM != 2 && hup != nullptr && valid) ? hup[chain] : 0.f;
+    double lz2 = BM ? 0.0 : saved_lz[bb];
 
     MT lc[G][K];
     float pc[G][K];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int a = 0; a < K; ++a) { lc[g][a] = (MT)0; pc[g][a] = 0.f; }
     double N = 0.0;
+    if constexpr (BM == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) { lc[g][a] = (MT)0; pc[g][a] = 0.f; }
+    } else if constexpr (BM == 1) {
+      const double* l0 = sa.lam0 + sg * M;
+      const float* f0 = sa.phi0 + sg * M;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          lc[g][a] = (MT)l0[p + g * LPS + a * NG];
+          pc[g][a] = f0[p + g * LPS + a * NG];
+        }
+      N = sa.sc0[sg * 2];
+    } else {
+      const long long i0 = bb % M;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          lc[g][a] = (p + g * LPS + a * NG == i0) ? (MT)0 : (MT)-kFar;
+          pc[g][a] = 0.f;
+        }
+    }
 
     // One forward step: (lam, Phi) column offsets of step t -> those of step t + 1 (t < L - 1).
     auto advance = [&](long long t) {
@@ -758,14 +801,76 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 
     // ---- phase A: lam and Phi, t = 0 .. L-1 ----------------------------------------------
     for (long long t = 0; t < L; ++t) {
-      if (seg == 0 || t % seg == 0) {
-        const long long e = seg ? t / seg : t;
-        store_vec<KG>(histl(e), &lc[0][0]);
-        store_vec<KG>(histp(e), &pc[0][0]);
+      if constexpr (BM != 2) {
+        if (seg == 0 || t % seg == 0) {
+          const long long e = seg ? t / seg : t;
+          store_vec<KG>(histl(e), &lc[0][0]);
+          store_vec<KG>(histp(e), &pc[0][0]);
+        }
+        if (p == 0) ns[t * SPB + q] = N;
       }
-      if (p == 0) ns[t * SPB + q] = N;
       if (t == L - 1) break;
       advance(t);
+    }
+    // One more step: lam and Phi at t1 = L, in butterfly order in the message buffer just
+    // written. They give the transfer and moment rows (BM 2), the segment's log2 Z (BM 1) and
+    // the posterior mean of the centred expectation at the last step (xbar, below).
+    float xbar = 0.f;
+    {
+      const double n_before = N;
+      advance(L - 1);
+      const double sh = N - n_before;
+      const MT* lm = msgl[C::DB ? mb ^ 1 : mb] + q * M;
+      const float* pm = msgp[C::DB ? mb ^ 1 : mb] + q * M;
+      if constexpr (BM == 2) {
+        if (valid) {
+          const long long ri = sg * M + bb % M;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              const int j = K * (p + g * LPS) + r;
+              sa.rows[ri * M + j] = (float)(lm[j] - (MT)sh);
+              sa.frows[ri * M + j] = pm[j];
+            }
+          if (p == 0) sa.rscale[ri] = N;
+        }
+        continue;  // transfer and moment rows need no backward sweep
+      } else {
+        // posterior weights of butterfly j at the last step, 2^(lam_L(j) + rho(j)), rho = 0 at a
+        // free end: their LSE is log2 Z (BM 1: N + Np0 + the LSE of the relative values), and
+        // the weighted mean of Phi_L(j) + Psi(j) is the mean xbar of the centred expectation
+        const double* r1 = BM == 1 ? sa.rho1 + sg * M : nullptr;
+        const float* s1 = BM == 1 ? sa.psi1 + sg * M : nullptr;
+        MT y[G][K];
+        MT mx = (MT)-INFINITY;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            const int j = K * (p + g * LPS) + r;
+            y[g][r] = lm[j] - (MT)sh;
+            if constexpr (BM == 1) y[g][r] += (MT)r1[j];
+            mx = tmax(mx, y[g][r]);
+          }
+        MT v1[1] = {mx};
+        chain_reduce<C, 1, 1u>(v1, red, rp);
+        float s2 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            const int j = K * (p + g * LPS) + r;
+            const float e = ex2((float)(y[g][r] - v1[0]));
+            s2 += e;
+            s3 = __builtin_fmaf(e, BM == 1 ? pm[j] + s1[j] : pm[j], s3);
+          }
+        float v2[2] = {s2, s3};
+        chain_reduce<C, 2, 0u>(v2, red, rp);
+        if constexpr (BM == 1)
+          lz2 = N + ((double)v1[0] + (double)lg2(v2[0])) + sa.sc0[sg * 2 + 1];
+        xbar = v2[1] / v2[0];
+      }
     }
     __syncthreads();
 
@@ -774,11 +879,24 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
     // when the history is checkpointed (one segment of length L otherwise).
     MT rr[G][K];
     float qr[G][K];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int r = 0; r < K; ++r) { rr[g][r] = (MT)0; qr[g][r] = 0.f; }
     double Np = 0.0;
+    if constexpr (BM == 1) {
+      const double* r1 = sa.rho1 + sg * M;
+      const float* s1 = sa.psi1 + sg * M;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          rr[g][r] = (MT)r1[K * (p + g * LPS) + r];
+          qr[g][r] = s1[K * (p + g * LPS) + r];
+        }
+      Np = sa.sc0[sg * 2 + 1];
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < K; ++r) { rr[g][r] = (MT)0; qr[g][r] = 0.f; }
+    }
     const long long nseg = seg ? ncp : 1;
     for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
       const long long t0 = seg ? sgi * seg : 0;
@@ -821,7 +939,10 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int g = 0; g < G; ++g)
 #pragma unroll
           for (int r = 0; r < K; ++r) qrc[g][r] = qr[g][r] - gwh;
-        float gw = 0.f;
+        // E_t(s) = gamma (X - xbar + h) with X = Phi + g (c - w_hat) + Psi; xs sums it over the
+        // states, so xs - h is the part of the mean of X that xbar did not remove
+        const float hx = h - xbar;
+        float gw = 0.f, xs = 0.f;
         MT mx = (MT)-INFINITY;
         MT rout[G][K];
         float qout[G][K];
@@ -856,7 +977,8 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             qout[g][a] = ps * rcp_nr(cs);
             mx = tmax(mx, rout[g][a]);
             const float f = ex2((float)((m + lcur[g][a]) - LZ));
-            const float pa = pcur[g][a] + h;
+            const float pa = pcur[g][a] + hx;
+            xs = __builtin_fmaf(f, __builtin_fmaf(pa, cs, ps), xs);
             // (a uniform branch per 4x4 block: it also bounds the live ranges the scheduler
             // builds across blocks, which keeps this kernel at two waves per SIMD)
             if (valid) {
@@ -881,10 +1003,11 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
               pw[p + g * LPS + a * NG] = qout[g][a];
             }
         }
-        MT v2[2] = {(MT)gw, mx};
-        chain_reduce<C, 2, 2u>(v2, red, rp);
+        MT v2[3] = {(MT)gw, mx, (MT)xs};
+        chain_reduce<C, 3, 2u>(v2, red, rp);
+        xbar += (float)v2[2] - h;
         if (valid && p == 0)
-          grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+          grad_w[wofs + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
         if (t == 0) break;
         const MT sh = floor(v2[1]);
 #pragma unroll
@@ -904,6 +1027,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 
   // Codebook-gradient partial of this slot: combine the chains of the block (fixed xor order),
   // then one copy writes its states.
+  if constexpr (BM == 2) return;  // transfer and moment rows have no gradient part
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -1010,11 +1134,11 @@ int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   if (ckpt)
     hipLaunchKernelGGL((k_sparse_bwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
                        B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units,
-                       seg);
+                       seg, SegArgs{});
   else
     hipLaunchKernelGGL((k_sparse_bwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
                        B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units,
-                       seg);
+                       seg, SegArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((C::S + 255) / 256)), dim3(256), 0, st, partial,
@@ -1077,6 +1201,41 @@ int run_fwd_seg(const float* cb, const float* w, long long Bv, long long L, floa
   return run_fwd_seg_p<n, k, Fast, BM>(cb, w, Bv, L, T, w_hat, log_z, ws, sa, st);
 }
 
+// Segmented backward launches (BM 1: segments, writing codebook-gradient partials of `grid`
+// slots at `partial`; BM 2: transfer and moment rows). No slot reduction here: the caller sums
+// the partials of every launch once.
+template <int n, int k, class P, int BM>
+int run_bwd_seg_p(const float* cb, const float* w, long long Bv, long long L, float T,
+                  const float* w_hat, const float* gup, const float* hup, float* grad_w,
+                  float* partial, void* ws, const SegArgs& sa, int* grid_used, hipStream_t st) {
+  SparseGeom g;
+  if (!sparse_geom(n, k, Bv, bwd_kind<P>(), &g)) return (int)hipErrorInvalidValue;
+  using C = Cfg<(1 << k), geom_g(n, k, bwd_kind<P>()), geom_lps(n, k, bwd_kind<P>()), P, true>;
+  if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
+  const Consts kc = make_consts(T, P::kPrecise);
+  const size_t slot = BM == 2 ? 0 : sparse_bwd_slot_bytes(g, L, false);
+  const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_bwd<C, false, BM>),
+                                 C::BLOCK, g.slots);
+  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+  *grid_used = grid;
+  hipLaunchKernelGGL((k_sparse_bwd<C, false, BM>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb,
+                     w, Bv, L, kc, (const double*)nullptr, w_hat, gup, hup, grad_w, partial, ws,
+                     slot, (long long)g.units, 0LL, sa);
+  return (int)hipGetLastError();
+}
+
+template <int n, int k, int BM>
+int run_bwd_seg(const float* cb, const float* w, long long Bv, long long L, float T,
+                const float* w_hat, const float* gup, const float* hup, float* grad_w,
+                float* partial, void* ws, const SegArgs& sa, int* grid_used, hipStream_t st) {
+  if constexpr (precise_fits<n, k>())
+    if (use_precise<n, k>(T))
+      return run_bwd_seg_p<n, k, Precise, BM>(cb, w, Bv, L, T, w_hat, gup, hup, grad_w, partial,
+                                              ws, sa, grid_used, st);
+  return run_bwd_seg_p<n, k, Fast, BM>(cb, w, Bv, L, T, w_hat, gup, hup, grad_w, partial, ws, sa,
+                                       grid_used, st);
+}
+
 }  // namespace
 
 // Instantiated shapes: see geom_supported().
@@ -1132,7 +1291,7 @@ int launch_sparse_forward_seg(int mode, int n, int k, const float* codebook, con
                               const SegLaunch& sl, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const SegArgs sa{sl.nseg, sl.jbase, sl.seglen, sl.lfull, sl.ptot, sl.lam0, sl.rho1, sl.sc0,
-                   sl.rows, sl.rscale};
+                   sl.rows, sl.rscale, nullptr, nullptr, nullptr};
 #define X(N_, K_)                                                                            \
   if (n == N_ && k == K_)                                                                    \
     return mode == 2 ? run_fwd_seg<N_, K_, 2>(codebook, w, Bv, L, T, w_hat, log_z, ws, sa, st) \
@@ -1140,6 +1299,33 @@ int launch_sparse_forward_seg(int mode, int n, int k, const float* codebook, con
   BCJR_SCAN_SHAPES(X)
 #undef X
   return (int)hipErrorInvalidValue;
+}
+
+int launch_sparse_backward_seg(int mode, int n, int k, const float* codebook, const float* w,
+                               int64_t Bv, int64_t L, float T, const float* w_hat,
+                               const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                               float* partial, void* ws, const SegLaunch& sl, int* grid_used,
+                               void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SegArgs sa{sl.nseg, sl.jbase, sl.seglen, sl.lfull, sl.ptot, sl.lam0, sl.rho1, sl.sc0,
+                   sl.rows, sl.rscale, sl.phi0, sl.psi1, sl.frows};
+#define X(N_, K_)                                                                          \
+  if (n == N_ && k == K_)                                                                  \
+    return mode == 2 ? run_bwd_seg<N_, K_, 2>(codebook, w, Bv, L, T, w_hat, grad_w_hat,    \
+                                              grad_log_z, grad_w, partial, ws, sa,         \
+                                              grid_used, st)                               \
+                     : run_bwd_seg<N_, K_, 1>(codebook, w, Bv, L, T, w_hat, grad_w_hat,    \
+                                              grad_log_z, grad_w, partial, ws, sa,         \
+                                              grid_used, st);
+  BCJR_SCAN_SHAPES(X)
+#undef X
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_reduce_slots(const float* partial, int64_t slots, int S, float* out, void* stream) {
+  hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((S + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), partial, (long long)slots, (long long)S, out);
+  return (int)hipGetLastError();
 }
 
 bool scan_shape_built(int n, int k) {

@@ -31,7 +31,8 @@ METRIC = "BCJR fwd+bwd trellis state-steps/sec (1 MI355X) + % of HBM/compute roo
 # operations per trellis state-step of the butterfly-factorised forward-backward. Counted from
 # the recursions, not from the compiled code; an FMA counts as one operation.
 #   forward  kernel: alpha side 4.5 VALU + 1.25 trans, beta side + posterior + w_hat 6.5 + 1.5
-#   backward kernel: alpha side + Phi 7.25 VALU + 1.5 trans, beta side + Psi + D + grads 15 + 1.75
+#   backward kernel: alpha side + Phi 7.25 VALU + 1.5 trans, beta side + Psi + D + grads 15.5 + 1.75
+#   (incl. 0.5 for the running posterior mean that re-centres the conditional expectations)
 # Peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T VALU lane-op slots/s (one wave64
 # instruction per SIMD per 4 clocks; the 157.3 TFLOP/s fp32 figure is this rate x 4 flops of a
 # packed dual FMA, which this build does not use). Transcendentals (v_exp_f32, v_log_f32,
@@ -40,7 +41,7 @@ METRIC = "BCJR fwd+bwd trellis state-steps/sec (1 MI355X) + % of HBM/compute roo
 # ---------------------------------------------------------------------------------------------
 OPS = {
     "fwd": {"valu": 4.5 + 6.5, "trans": 1.25 + 1.5},
-    "bwd": {"valu": 7.25 + 15.0, "trans": 1.5 + 1.75},
+    "bwd": {"valu": 7.25 + 15.5, "trans": 1.5 + 1.75},
 }
 TRANS_SLOTS = 2.0
 PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12

@@ -145,8 +145,7 @@ bcjr_status viterbi_decode(const bcjr_trellis* tr, const float* w, int64_t B, in
  * double precision, and every segment runs its forward-backward from its boundary messages.
  * Phase 1 costs S/K times the forward recursion's work, so this pays where chains are too few
  * to fill the device and L is long (e.g. one chain of 2^20 steps at S = 256: ~300x faster
- * than bcjr_forward; at S = 4096 it is not faster). No backward: the result is the forward's
- * w_hat and log Z only.
+ * than bcjr_forward; at S = 4096 it is not faster). Its backward is bcjr_backward_scan below.
  *
  * seg_len  segment length in steps, > 0, or 0 for the default, about sqrt(L) steps scaled by
  *          the boundary scan's cost per segment (which grows with (S/K)^2), at least 16;
@@ -169,6 +168,32 @@ size_t bcjr_scan_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, i
 bcjr_status bcjr_forward_scan(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
                               float T, int64_t seg_len, float* w_hat, float* log_z, void* ws,
                               size_t ws_bytes, bcjr_stream_t stream);
+
+/*
+ * Segmented backward: the gradient of F = sum g * w_hat + sum h * log_z (as bcjr_backward,
+ * "exactly differentiable", abstract) with parallelism along the chain. The centred conditional
+ * expectations the gradient is built from (Phi forward, Psi backward) compose over a segment
+ * through its moment matrix F(i, j) = E[sum over the segment of g_u (c(s_u) - w_hat_u) |
+ * butterfly i at its start, j at its end]: phase 1 forms the transfer and moment rows from
+ * S/K one-hot starts per segment, phase 2 scans messages and expectations over the segments,
+ * phase 3 runs every segment's backward from its boundary values. Same shapes, defaults and
+ * cost profile as bcjr_forward_scan.
+ * w_hat      DEVICE [B,L] the soft codeword from bcjr_forward_scan (or bcjr_forward) with the
+ *            same w, T and codebook, read only (it centres the expectations)
+ * grad_w_hat DEVICE [B,L] upstream gradient g
+ * grad_log_z DEVICE [B] upstream gradient h, or NULL for h = 0
+ * grad_w     DEVICE [B,L] written
+ * grad_codebook DEVICE [S] written (overwritten, summed over all chains; zero for B = 0)
+ * ws         DEVICE, ws_bytes >= bcjr_scan_backward_workspace_bytes(tr, B, L, seg_len)
+ * Any seg_len may be used (it need not equal the forward's).
+ */
+size_t bcjr_scan_backward_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L,
+                                          int64_t seg_len);
+bcjr_status bcjr_backward_scan(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                               float T, int64_t seg_len, const float* w_hat,
+                               const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                               float* grad_codebook, void* ws, size_t ws_bytes,
+                               bcjr_stream_t stream);
 
 /* ---- Hard-code export (bitshift trellis) ------------------------------------------------------
  * The zero-temperature end of the method: the hard code that the abstract says is recovered as

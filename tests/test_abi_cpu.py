@@ -290,3 +290,26 @@ def test_scan_rejects_bad_arguments_without_device(lib):
     assert scan(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
     assert scan(ws=0x6008) == bcjr.BCJR_E_WORKSPACE
     assert scan(B=0, w=0, wh=0, lz=0, ws=0, wsb=0) == bcjr.BCJR_OK
+
+
+def test_scan_backward_rejects_bad_arguments_without_device(lib):
+    P = ctypes.c_void_p
+
+    def bscan(n=8, cb=0x1000, w=0x2000, B=2, L=64, T=0.5, seg=16, wh=0x3000, g=0x4000, gw=0x5000,
+              gc=0x7000, ws=0x6000, wsb=1 << 40):
+        tr = bcjr.Trellis(n, 2, 1, cb)
+        return lib.bcjr_backward_scan(ctypes.byref(tr), P(w), B, L, T, seg, P(wh), P(g), None,
+                                      P(gw), P(gc), P(ws), wsb, None)
+
+    assert bscan(seg=-1) == bcjr.BCJR_E_ARG
+    assert bscan(T=0.0) == bcjr.BCJR_E_ARG
+    assert bscan(gc=0) == bcjr.BCJR_E_ARG
+    assert bscan(wh=0) == bcjr.BCJR_E_ARG
+    assert bscan(g=0) == bcjr.BCJR_E_ARG
+    assert bscan(gw=0) == bcjr.BCJR_E_ARG
+    assert bscan(n=13) == bcjr.BCJR_E_UNSUPPORTED
+    need = bcjr.bcjr_scan_backward_workspace_bytes(8, 2, 2, 64, 16)
+    assert need > bcjr.bcjr_scan_workspace_bytes(8, 2, 2, 64, 16)   # moment rows and partials
+    assert bscan(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
+    assert bscan(ws=0x6008) == bcjr.BCJR_E_WORKSPACE
+    assert bcjr.bcjr_scan_backward_workspace_bytes(8, 2, 0, 64, 16) == 0

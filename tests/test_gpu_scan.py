@@ -1,12 +1,12 @@
-"""The segmented (parallel-in-L) forward for long chains against the oracle's sequential
-forward-backward and against the GPU's sequential forward."""
+"""The segmented (parallel-in-L) forward and backward for long chains against the oracle's
+sequential forward-backward and gradient, and against the GPU's sequential entry points."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from bcjr_soft_decoding_amd import bcjr, synth
-from tests.gpu_helpers import RTOL_FWD, assert_normwise, assert_rel, dev, log_case
+from tests.gpu_helpers import RTOL_FWD, RTOL_GRAD, assert_normwise, assert_rel, dev, log_case
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +101,50 @@ def test_scan_full_workload_in_bench_configuration():
     ref = oracle.sparse_forward(wl.n, wl.k, c, w, T)
     assert_normwise(wh.cpu().numpy(), ref["w_hat"], RTOL_FWD, "w_hat vs oracle")
     assert_rel(lz.cpu().numpy(), ref["log_z"], RTOL_FWD, "log_z vs oracle")
+
+
+@pytest.mark.parametrize("n,B,L,seg,T", CASES)
+def test_scan_backward_matches_oracle_and_sequential(n, B, L, seg, T):
+    k = 2
+    c = synth.normal(11000 + n, (1 << n,))
+    w = synth.normal(11100 + n + L, (B, L))
+    g = synth.normal(11500 + n + L, (B, L))
+    h = synth.normal(11600 + n + L, (B,)) if B % 2 else None   # with and without the log-Z term
+    used = bcjr.bcjr_scan_segment_length(n, k, B, L, seg)
+    log_case(f"scan bwd n={n} B={B} L={L} seg={seg} (used {used}) T={T} h={h is not None}")
+    cd, wd, gd = dev(c), dev(w), dev(g)
+    hd = None if h is None else dev(h)
+    wh, _ = bcjr.bcjr_forward_scan(cd, wd, n, k, T, seg)
+    gw, gc = bcjr.bcjr_backward_scan(cd, wd, n, k, T, wh, gd, hd, seg)
+    _, _, saved = bcjr.bcjr_forward(cd, wd, n, k, T)
+    gw2, gc2 = bcjr.bcjr_backward(cd, wd, n, k, T, saved, gd, hd)
+    torch.cuda.synchronize()
+    rb = oracle.sparse_backward(n, k, c, w, T, g, h)
+    assert_normwise(gw.cpu().numpy(), rb["grad_w"], RTOL_GRAD, "grad_w vs oracle")
+    assert_normwise(gc.cpu().numpy(), rb["grad_codebook"], RTOL_GRAD, "grad_c vs oracle")
+    assert_normwise(gw.cpu().numpy(), gw2.cpu().numpy(), RTOL_GRAD, "grad_w vs sequential")
+    assert_normwise(gc.cpu().numpy(), gc2.cpu().numpy(), RTOL_GRAD, "grad_c vs sequential")
+
+
+def test_scan_backward_zero_chains_zeroes_the_codebook_gradient():
+    c = dev(synth.normal(11700, (256,)))
+    w = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    log_case("scan bwd B=0")
+    gc = torch.full((256,), 7.0, device="cuda")
+    bcjr.bcjr_backward_scan(c, w, 8, 2, 0.5, w, w, None, 16, grad_codebook=gc)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gc).item() == 0
+
+
+def test_scan_backward_long_chain_against_oracle():
+    n, k, L, T = 8, 2, 1 << 16, 0.1
+    c = synth.normal(11800, (1 << n,))
+    w = synth.normal(11801, (1, L))
+    g = synth.normal(11802, (1, L))
+    log_case(f"scan bwd long chain n={n} L={L}")
+    wh, _ = bcjr.bcjr_forward_scan(dev(c), dev(w), n, k, T)
+    gw, gc = bcjr.bcjr_backward_scan(dev(c), dev(w), n, k, T, wh, dev(g))
+    torch.cuda.synchronize()
+    rb = oracle.sparse_backward(n, k, c, w, T, g)
+    assert_normwise(gw.cpu().numpy(), rb["grad_w"], RTOL_GRAD, "grad_w")
+    assert_normwise(gc.cpu().numpy(), rb["grad_codebook"], RTOL_GRAD, "grad_c")
