@@ -102,7 +102,7 @@ def parse():
                     help="time the hard-code export (pack / unpack of Viterbi paths) instead")
     ap.add_argument("--seg-len", type=int, default=0,
                     help="segment length of the segmented forward (workload 6); 0 = default")
-    ap.add_argument("--cpu-scan-steps", type=int, default=1 << 18,
+    ap.add_argument("--cpu-scan-steps", type=int, default=1 << 17,
                     help="chain steps timed on the CPU oracle for workload 6")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
@@ -307,26 +307,31 @@ def bench_export(args, wl):
     }))
 
 
-# Segmented forward of long chains (parallel in L): phase 1 runs the forward (alpha) recursion
-# from S/K one-hot starts per segment (alpha side: 4.5 VALU + 1.25 trans = 7.0 slots per
-# state-step, over L * S * S/K state-steps), phase 3 the full forward over L * S state-steps
-# (16.5 slots); the boundary scan between them does O(segments * (S/K)^2) work, counted as 0.
-SCAN_PHASE1_SLOTS = 4.5 + 1.25 * TRANS_SLOTS
+# Segmented forward-backward of long chains (parallel in L). Algorithmic ALU work per call:
+#   forward : phase 1 runs the alpha recursion from S/K one-hot starts per segment (alpha side:
+#             4.5 VALU + 1.25 trans = 7.0 slots per state-step over L * S * S/K state-steps),
+#             phase 3 the full forward over L * S state-steps (16.5 slots);
+#   backward: phase 1 runs the alpha + Phi recursion from the one-hot starts (7.25 VALU + 1.5
+#             trans = 10.25 slots over L * S * S/K), phase 3 the full backward (29.25 slots).
+# The boundary scans between them do O(segments * (S/K)^2) work, counted as 0.
+SCAN_FWD_ROW_SLOTS = 4.5 + 1.25 * TRANS_SLOTS
+SCAN_BWD_ROW_SLOTS = 7.25 + 1.5 * TRANS_SLOTS
 
 
-def cpu_baseline_scan(wl, c, w, T, steps):
+def cpu_baseline_scan(wl, c, w, g, T, steps):
     import oracle
     cores = oracle.set_threads(0)
     t0 = time.perf_counter()
     oracle.sparse_forward(wl.n, wl.k, c, w[:, :steps], T)
+    oracle.sparse_backward(wl.n, wl.k, c, w[:, :steps], T, g[:, :steps])
     dt = time.perf_counter() - t0
     return {
         "value": wl.B * steps * wl.S / dt,
         "unit": "state-steps/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"first {steps} of {wl.L} steps of the chain (S={wl.S}), fp64 oracle forward "
-                  f"(sequential in L; one chain runs on one thread), {dt:.1f} s",
+        "sample": f"first {steps} of {wl.L} steps of the chain (S={wl.S}), fp64 oracle forward + "
+                  f"backward (sequential in L; one chain runs on one thread), {dt:.1f} s",
     }
 
 
@@ -340,37 +345,55 @@ def bench_scan(args, wl):
     M = S >> k
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c_np, w_np = synth.codebook(wl.index), synth.weights(wl.index)
-    c, w = torch.from_numpy(c_np).to(dev), torch.from_numpy(w_np).to(dev)
+    c_np, w_np, g_np = synth.codebook(wl.index), synth.weights(wl.index), synth.upstream_grad(wl.index)
+    c, w, g = (torch.from_numpy(a).to(dev) for a in (c_np, w_np, g_np))
     seg = bcjr.bcjr_scan_segment_length(n, k, B, L, args.seg_len)
-    ws = torch.empty(bcjr.bcjr_scan_workspace_bytes(n, k, B, L, seg), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(bcjr.bcjr_scan_workspace_bytes(n, k, B, L, seg), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bcjr.bcjr_scan_backward_workspace_bytes(n, k, B, L, seg), dtype=torch.uint8,
+                      device=dev)
     w_hat = torch.empty_like(w)
     log_z = torch.empty(B, dtype=torch.float32, device=dev)
+    grad_w = torch.empty_like(w)
+    grad_c = torch.empty_like(c)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bcjr.bcjr_forward_scan(c, w, n, k, T, seg, w_hat, log_z, wsf)
+        if ev is not None:
+            ev[1].record()
+        bcjr.bcjr_backward_scan(c, w, n, k, T, w_hat, g, None, seg, grad_w, grad_c, wsb)
+        if ev is not None:
+            ev[2].record()
+
     for _ in range(args.warmup):
-        bcjr.bcjr_forward_scan(c, w, n, k, T, seg, w_hat, log_z, ws)
+        step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in ev:
-        e[0].record()
-        bcjr.bcjr_forward_scan(c, w, n, k, T, seg, w_hat, log_z, ws)
-        e[1].record()
+        step(e)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    assert torch.isfinite(w_hat).all() and torch.isfinite(log_z).all()
-    # the sequential forward on the same chain, for reference (one untimed warm-up)
-    wh2, lz2, _ = bcjr.bcjr_forward(c, w, n, k, T)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    assert torch.isfinite(w_hat).all() and torch.isfinite(grad_w).all() and torch.isfinite(grad_c).all()
+    # the sequential entry points on the same chain, for reference (one untimed warm-up each)
+    wh2, lz2, saved = bcjr.bcjr_forward(c, w, n, k, T)
+    gw2, gc2 = bcjr.bcjr_backward(c, w, n, k, T, saved, g)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    bcjr.bcjr_forward(c, w, n, k, T, wh2, lz2)
+    bcjr.bcjr_forward(c, w, n, k, T, wh2, lz2, saved)
+    bcjr.bcjr_backward(c, w, n, k, T, saved, g, None, gw2, gc2)
     torch.cuda.synchronize()
     seq_ms = (time.perf_counter() - t1) * 1e3
-    diff = float((w_hat - wh2).abs().max() / wh2.abs().max())
-    slots = SCAN_PHASE1_SLOTS * L * S * M * B + op_slots("fwd") * L * S * B
-    achieved = slots / (call_ms * 1e-3) / 1e12
+    diff_w = float((w_hat - wh2).abs().max() / wh2.abs().max())
+    diff_g = float((grad_w - gw2).abs().max() / gw2.abs().max())
+    fslots = SCAN_FWD_ROW_SLOTS * L * S * M * B + op_slots("fwd") * L * S * B
+    bslots = SCAN_BWD_ROW_SLOTS * L * S * M * B + op_slots("bwd") * L * S * B
+    ach_b = bslots / (bwd_ms * 1e-3) / 1e12
     out = {
-        "metric": "segmented BCJR forward (parallel in L) trellis state-steps/sec (1 MI355X)",
+        "metric": "segmented BCJR fwd+bwd (parallel in L) trellis state-steps/sec (1 MI355X)",
         "value": B * L * S / (elapsed / args.steps),
         "unit": "state-steps/s",
         "n_gpus": 1,
@@ -384,24 +407,26 @@ def bench_scan(args, wl):
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "L": L, "S": S, "k": k, "T": T,
                    "segment_length": seg, "segments": -(-L // seg),
-                   "workspace_bytes": int(ws.numel()), "parallelism": "single-gpu"},
-        "sequential_forward_ms": seq_ms,
+                   "workspace_bytes": int(wsf.numel() + wsb.numel()), "parallelism": "single-gpu"},
+        "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
+        "sequential_fwd_bwd_ms": seq_ms,
         "speedup_vs_sequential": seq_ms / (elapsed * 1e3 / args.steps),
-        "max_rel_diff_vs_sequential": diff,
+        "max_rel_diff_vs_sequential": {"w_hat": diff_w, "grad_w": diff_g},
         "roofline": {
             "bound": "alu",
-            "kernel": "bcjr_forward_scan (k_sparse_fwd transfer rows + k_scan_bounds + "
-                      "k_sparse_fwd segments)",
-            "achieved": achieved,
+            "kernel": "bcjr_backward_scan (k_sparse_bwd transfer/moment rows + k_scan_bounds + "
+                      "k_sparse_bwd segments + k_reduce_slots)",
+            "achieved": ach_b,
             "peak": PEAK_TOPS,
             "unit": "Tops/s",
-            "frac": achieved / PEAK_TOPS,
-            "slots_per_launch": slots,
+            "frac": ach_b / PEAK_TOPS,
+            "slots_per_launch": bslots,
+            "forward_frac": fslots / (fwd_ms * 1e-3) / 1e12 / PEAK_TOPS,
             "traffic": None,
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_scan(wl, c_np, w_np, T, min(args.cpu_scan_steps, L))
+        out["cpu_baseline"] = cpu_baseline_scan(wl, c_np, w_np, g_np, T, min(args.cpu_scan_steps, L))
     print(json.dumps(out))
 
 
