@@ -26,7 +26,7 @@
 // Precision policies. The messages lam and rho are sums along the trellis of emission terms
 // whose size grows like 1/T. In fp32 their accumulated rounding (about an ulp of a value of
 // size log2(e)/T per step) limits the gradient, whose sensitivity to posterior errors is
-// large when T is small, so below T = 0.05 the messages are carried in fp64 and the emission
+// large when T is small, so below T = 0.01 the messages are carried in fp64 and the emission
 // is formed from the unscaled difference w - c; exponentials, the posterior weights and the
 // conditional expectations stay fp32 in both policies. The 2^16-state trellis keeps fp32
 // messages at every T: its fp64 backward messages would not fit in LDS.
@@ -1058,7 +1058,7 @@ k_reduce_slots(const float* __restrict__ partial, long long slots, long long cou
 // message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS. The fp64-message
 // kernels use their own lane geometry (kFwdP / kBwdP): fewer states per lane, since every
 // message takes two registers.
-constexpr float kPreciseBelowT = 0.05f;
+constexpr float kPreciseBelowT = 0.01f;
 template <int n, int k>
 constexpr bool precise_fits() {
   return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;

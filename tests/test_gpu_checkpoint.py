@@ -38,9 +38,9 @@ CASES = [
     (6, 2, 1, 0.5),      # L = 1
     (6, 3, 2, 0.5),
     (16, 2, 20, 0.3),    # 16-wave chains
-    (8, 4, 64, 0.01),    # fp64 messages
-    (12, 2, 60, 0.02),   # fp64 messages, workload-3 size
-    (14, 2, 20, 0.02),   # fp64 messages, 1024-lane chains
+    (8, 4, 64, 0.005),   # fp64 messages
+    (12, 2, 60, 0.005),  # fp64 messages, workload-3 size
+    (14, 2, 20, 0.005),  # fp64 messages, 1024-lane chains
 ]
 
 

@@ -88,7 +88,7 @@ def test_all_state_sizes(n):
 
 @pytest.mark.parametrize("n", list(range(4, 16)))
 def test_all_state_sizes_fp64_messages(n):
-    """T below 0.05: the fp64-message kernels (their own lane geometry) for every size that
+    """T below 0.01: the fp64-message kernels (their own lane geometry) for every size that
     has them (the 2^16-state trellis keeps fp32 messages)."""
     B = 3 if n < 15 else 2
     L = 13
@@ -96,7 +96,7 @@ def test_all_state_sizes_fp64_messages(n):
     w = synth.normal(410 + n, (B, L))
     g = synth.normal(510 + n, (B, L))
     h = synth.normal(610 + n, (B,))
-    _compare(n, 2, c, w, 0.02, g, h, "sizes-fp64")
+    _compare(n, 2, c, w, 0.005, g, h, "sizes-fp64")
 
 
 # ------------------------------------------------------------------------------------------

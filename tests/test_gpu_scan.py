@@ -22,7 +22,7 @@ CASES = [
     (8, 3, 1000, 64, 0.1),     # ragged tail segment
     (4, 5, 333, 16, 1.0),      # S = 16, many segments
     (6, 2, 500, 2, 0.3),       # segments shorter than n/k: transfer rows with unreachable states
-    (8, 2, 777, 100, 0.02),    # fp64 messages
+    (8, 2, 777, 100, 0.005),   # fp64 messages
     (12, 1, 1200, 256, 0.1),   # S = 4096 (M = 1024)
     (10, 2, 1500, 0, 0.2),     # default segment length
     (8, 2, 100, 1000, 0.5),    # one segment (seg >= L)
