@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1536, help="chains timed on the CPU oracle")
     ap.add_argument("--cpu-sample-dense", type=int, default=64,
                     help="chains of the dense workload timed on the CPU oracle")
+    ap.add_argument("--viterbi", action="store_true",
+                    help="time the Viterbi decoder (the T -> 0 limit) on the workload instead")
     ap.add_argument("--export", action="store_true",
                     help="time the hard-code export (pack / unpack of Viterbi paths) instead")
     ap.add_argument("--seg-len", type=int, default=0,
@@ -120,6 +122,16 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, c, w, g, T, sample):
     import oracle
     cores = oracle.set_threads(0)
@@ -129,6 +141,14 @@ def cpu_baseline(wl, c, w, g, T, sample):
     oracle.sparse_forward(wl.n, wl.k, c, ws, T)
     oracle.sparse_backward(wl.n, wl.k, c, ws, T, gs)
     dt = time.perf_counter() - t0
+    # the same work on one thread, on a sixteenth of the sample
+    s1 = max(1, sample // 16)
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    oracle.sparse_forward(wl.n, wl.k, c, w[:s1], T)
+    oracle.sparse_backward(wl.n, wl.k, c, w[:s1], T, g[:s1])
+    d1 = time.perf_counter() - t1
+    oracle.set_threads(cores)
     return {
         "value": sample * wl.L * wl.S / dt,
         "unit": "state-steps/s",
@@ -136,6 +156,8 @@ def cpu_baseline(wl, c, w, g, T, sample):
         "kind": "oracle",
         "sample": f"first {sample} of {wl.B} chains (L={wl.L}, S={wl.S}), fp64 oracle forward + "
                   f"backward, {dt:.1f} s on {cores} OpenMP threads",
+        "value_1thread": s1 * wl.L * wl.S / d1,
+        "cpu_model": cpu_model(),
     }
 
 
@@ -170,6 +192,7 @@ def cpu_baseline_dense(wl, th, c, w, g, T, sample):
         "kind": "oracle",
         "sample": f"first {sample} of {wl.B} chains (L={wl.L}, S={wl.S} dense), fp64 oracle "
                   f"forward + backward incl. theta gradient, {dt:.1f} s on {cores} OpenMP threads",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -332,6 +355,7 @@ def cpu_baseline_scan(wl, c, w, g, T, steps):
         "kind": "oracle",
         "sample": f"first {steps} of {wl.L} steps of the chain (S={wl.S}), fp64 oracle forward + "
                   f"backward (sequential in L; one chain runs on one thread), {dt:.1f} s",
+        "cpu_model": cpu_model(),
     }
 
 
@@ -430,6 +454,67 @@ def bench_scan(args, wl):
     print(json.dumps(out))
 
 
+# Viterbi: per state-step (K = 4) a candidate costs sub + mul + add, and 3 of the K candidates a
+# compare and two selects (value, index) for the first strict minimum: 5.25 VALU; backpointers
+# 1 byte per butterfly = 0.25 B of HBM writes per state-step. ALU-bound (21 ops/B > ~5).
+VIT_SLOTS = 5.25
+
+
+def bench_viterbi(args, wl):
+    import numpy as np
+    import torch
+
+    from bcjr_soft_decoding_amd import bcjr, synth
+    n, k, B, L, S = wl.n, wl.k, wl.B, wl.L, wl.S
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c_np, w_np = synth.codebook(wl.index), synth.weights(wl.index)
+    c, w = torch.from_numpy(c_np).to(dev), torch.from_numpy(w_np).to(dev)
+    states = torch.empty((B, L), dtype=torch.int32, device=dev)
+    w_hard = torch.empty_like(w)
+    ws = bcjr.workspace(n, k, B, L, bcjr.VIT, dev)
+    for _ in range(args.warmup):
+        bcjr.viterbi_decode(c, w, n, k, states, w_hard, ws=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        bcjr.viterbi_decode(c, w, n, k, states, w_hard, ws=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    achieved = VIT_SLOTS * B * L * S / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "Viterbi decode trellis state-steps/sec (1 MI355X)",
+        "value": B * L * S / (elapsed / args.steps), "unit": "state-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "-viterbi", "B": B, "L": L, "S": S, "k": k,
+                   "workspace_bytes": int(ws.numel()), "parallelism": "single-gpu"},
+        "kernels_ms": {"viterbi": ms},
+        "roofline": {"bound": "alu", "kernel": "k_viterbi", "achieved": achieved, "peak": PEAK_TOPS,
+                     "unit": "Tops/s", "frac": achieved / PEAK_TOPS,
+                     "ops_per_state_step": VIT_SLOTS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = oracle.set_threads(0)
+        sample = min(args.cpu_sample, B)
+        t1 = time.perf_counter()
+        ref = oracle.viterbi(n, k, c_np, w_np[:sample])
+        dt = time.perf_counter() - t1
+        assert np.array_equal(ref["states"], states[:sample].cpu().numpy()), "Viterbi paths differ"
+        out["cpu_baseline"] = {
+            "value": sample * L * S / dt, "unit": "state-steps/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"first {sample} of {B} chains (L={L}, S={S}), fp32 oracle Viterbi "
+                      f"(paths checked equal to the GPU's), {dt:.1f} s on {cores} OpenMP threads"}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -451,6 +536,10 @@ def main():
         if wl.dense:
             raise SystemExit("the hard-code export is defined for the bitshift trellis")
         return bench_export(args, wl)
+    if args.viterbi:
+        if wl.dense:
+            raise SystemExit("the Viterbi decoder is defined for the bitshift trellis")
+        return bench_viterbi(args, wl)
     if wl.dense:
         return bench_dense(args, wl)
     if wl.index == 6:
