@@ -46,6 +46,7 @@ class QATConfig:
     steps: int = 100
     lr: float = 1e-4       # SGD step size eta
     r_voronoi: float = 1e-3
+    segmented: bool = False  # parallel-in-L entry points (for long chains, e.g. L = a whole row)
 
     def check(self):
         if self.steps < 1 or self.L < 1:
@@ -86,7 +87,8 @@ def step(w, W, X, codebook, cfg: QATConfig, T: float):
     """Loss and dloss/dw at the current latent weights (no update)."""
     R, C = W.shape
     wv = w.detach().requires_grad_(True)
-    w_hat, _ = autograd.soft_quantize(wv.reshape(-1, cfg.L), codebook, cfg.n, cfg.k, T)
+    w_hat, _ = autograd.soft_quantize(wv.reshape(-1, cfg.L), codebook, cfg.n, cfg.k, T,
+                                      segmented=cfg.segmented)
     loss = recon_loss(w_hat.reshape(R, C), W, X)
     grad, = torch.autograd.grad(loss, wv)
     return loss.detach(), grad
@@ -144,7 +146,7 @@ def run(rows: int, cols: int, samples: int, cfg: QATConfig, seed: int = 0, log_e
     out = {
         "rows": rows, "cols": cols, "samples": samples, "S": 1 << cfg.n, "k": cfg.k, "L": cfg.L,
         "chains": rows * cols // cfg.L, "t0": cfg.t0, "t_end": cfg.t_end, "steps": cfg.steps,
-        "lr": cfg.lr, "seed": seed,
+        "lr": cfg.lr, "seed": seed, "segmented": cfg.segmented,
         # output error per weight: recon_loss / (R C)
         "ptq_loss_calib": float(recon_loss(ptq_w, W, X)) / (rows * cols),
         "ptq_loss_heldout": float(recon_loss(ptq_w, W, Xv)) / (rows * cols),
@@ -175,10 +177,13 @@ def main(argv=None):
     ap.add_argument("--lr", type=float, nargs="+", default=[1e-4])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--log-every", type=int, default=0)
+    ap.add_argument("--segmented", action="store_true",
+                    help="use the parallel-in-L soft quantiser (long chains, e.g. --L = --cols)")
     a = ap.parse_args(argv)
     for lr in a.lr:
         for t0 in a.t0:
-            cfg = QATConfig(n=a.n, k=a.k, L=a.L, t0=t0, t_end=a.t_end, steps=a.steps, lr=lr)
+            cfg = QATConfig(n=a.n, k=a.k, L=a.L, t0=t0, t_end=a.t_end, steps=a.steps, lr=lr,
+                            segmented=a.segmented)
             print(json.dumps(run(a.rows, a.cols, a.samples, cfg, a.seed, a.log_every)), flush=True)
 
 

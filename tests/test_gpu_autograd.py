@@ -76,3 +76,30 @@ def test_dense_soft_quantize_matches_oracle():
     assert_normwise(wd.grad.cpu().numpy(), rb["grad_w"], RTOL_GRAD, "grad_w")
     assert_normwise(cd.grad.cpu().numpy(), rb["grad_codebook"], RTOL_GRAD, "grad_c")
     assert_normwise(td.grad.cpu().numpy(), rb["grad_theta"], RTOL_GRAD, "grad_theta")
+
+
+def test_segmented_soft_quantize_matches_sequential():
+    """soft_quantize(segmented=True) on long chains: the same values and gradients as the
+    ordinary wrapper (rel 1e-4 / 1e-3), and the oracle's."""
+    n, k, T = 8, 2, 0.2
+    c = synth.normal(8300, (1 << n,))
+    w = synth.normal(8301, (2, 5000))
+    g = synth.normal(8302, (2, 5000))
+    h = synth.normal(8303, (2,))
+    log_case("autograd segmented n=8 [2,5000]")
+    outs = []
+    for seg in (True, False):
+        wd = dev(w).requires_grad_(True)
+        cd = dev(c).requires_grad_(True)
+        w_hat, log_z = autograd.soft_quantize(wd, cd, n, k, T, segmented=seg, seg_len=128)
+        ((w_hat * dev(g)).sum() + (log_z * dev(h)).sum()).backward()
+        torch.cuda.synchronize()
+        outs.append((w_hat.detach().cpu().numpy(), log_z.detach().cpu().numpy(),
+                     wd.grad.cpu().numpy(), cd.grad.cpu().numpy()))
+    (a, lz, gw, gc), (a2, lz2, gw2, gc2) = outs
+    assert_normwise(a, a2, RTOL_FWD, "w_hat")
+    assert_normwise(gw, gw2, RTOL_GRAD, "grad_w")
+    assert_normwise(gc, gc2, RTOL_GRAD, "grad_c")
+    rb = oracle.sparse_backward(n, k, c, w, T, g, h)
+    assert_normwise(gw, rb["grad_w"], RTOL_GRAD, "grad_w vs oracle")
+    assert_normwise(gc, rb["grad_codebook"], RTOL_GRAD, "grad_c vs oracle")

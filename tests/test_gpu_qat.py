@@ -87,3 +87,18 @@ def test_hard_code_of_trained_weights_round_trips():
     np.testing.assert_array_equal(wh2.cpu().numpy().reshape(R, C), w_hard.cpu().numpy())
     ref = oracle.viterbi(n, 2, c, res.w.cpu().numpy().reshape(-1, L))
     np.testing.assert_array_equal(states.cpu().numpy(), ref["states"])
+
+
+def test_segmented_step_matches_oracle():
+    """One step with whole rows as chains through the parallel-in-L soft quantiser."""
+    n, R, C, N, T = 8, 2, 3000, 256, 0.2
+    log_case(f"qat segmented step n={n} R={R} C={C} (one chain per row)")
+    W, X, _, c = synth.qat_layer(R, C, N, n, seed=6)
+    rng = np.random.default_rng(3)
+    w = (W + 0.05 * rng.standard_normal(W.shape)).astype(np.float32)
+    cfg = qat.QATConfig(n=n, k=2, L=C, segmented=True)
+    loss, grad = qat.step(dev(w), dev(W), dev(X), dev(c), cfg, T)
+    torch.cuda.synchronize()
+    ref_loss, ref_g, _ = oqat.loss_and_grad(w, W, X, c, n, 2, C, T)
+    assert_rel(float(loss), ref_loss, RTOL_FWD, "loss")
+    assert_normwise(grad.cpu().numpy(), ref_g, RTOL_GRAD, "dloss/dw")
