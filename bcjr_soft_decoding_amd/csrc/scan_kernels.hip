@@ -248,6 +248,129 @@ k_scan_bounds(const float* __restrict__ rows, const double* __restrict__ rscale,
 #undef BCJR_LOAD_TILE
 }
 
+// ---------------------------------------------------------------------------------------------
+// The same scans for M <= 64 with one wave per chain and direction: lane l owns element l of the
+// boundary vectors and output l of each step, reductions are wave shuffles, and each segment's
+// rows (and moment rows) are staged in LDS with a padded stride (M + 1: the backward reads a row
+// per lane without bank conflicts) while the next segment's are loaded into registers.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWaveTile = 64 * 64 / 4 / 64;  // float4 per lane for a 64 x 64 tile
+
+__device__ __forceinline__ double wave_max(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int M, bool MOM>
+__global__ void __launch_bounds__(64)
+k_scan_wave(const float* __restrict__ rows, const double* __restrict__ rscale,
+            const float* __restrict__ frows, long long ptot, double* __restrict__ lam0,
+            double* __restrict__ rho1, double* __restrict__ sc0, float* __restrict__ phi0,
+            float* __restrict__ psi1) {
+  static_assert(M >= 4 && M <= 64, "one wave per chain and direction");
+  constexpr int RS = M + 1;
+  constexpr int nv = M * M / 4;  // float4 per tile
+  __shared__ float tq[M * RS];
+  __shared__ float tf[MOM ? M * RS : 1];
+  __shared__ float vin[M];
+  __shared__ float min_[M];
+  const long long c = blockIdx.x;
+  const bool fwd = blockIdx.y == 0;
+  const int l = threadIdx.x;
+  const bool own = l < M;
+  const long long nstep = ptot - 1;
+  auto seg_of = [&](long long q) { return c * ptot + (fwd ? q : ptot - 1 - q); };
+
+  double v = 0.0;   // boundary vector element l (log2, absolute)
+  float mom = 0.f;  // conditional expectation element l (MOM)
+  float4 rq[kWaveTile], rf[MOM ? kWaveTile : 1];
+  double rs = 0.0;
+#define BCJR_WAVE_LOAD(Q_)                                                                  \
+  do {                                                                                      \
+    const long long sg_ = seg_of(Q_);                                                       \
+    const float4* sq_ = reinterpret_cast<const float4*>(rows + sg_ * M * M);                \
+    _Pragma("unroll") for (int u_ = 0; u_ < kWaveTile; ++u_) {                              \
+      const int f_ = l + 64 * u_;                                                           \
+      rq[u_] = sq_[f_ < nv ? f_ : 0];                                                       \
+    }                                                                                       \
+    if constexpr (MOM) {                                                                    \
+      const float4* sf_ = reinterpret_cast<const float4*>(frows + sg_ * M * M);             \
+      _Pragma("unroll") for (int u_ = 0; u_ < kWaveTile; ++u_) {                            \
+        const int f_ = l + 64 * u_;                                                         \
+        rf[u_] = sf_[f_ < nv ? f_ : 0];                                                     \
+      }                                                                                     \
+    }                                                                                       \
+    rs = rscale[sg_ * M + (own ? l : 0)];                                                   \
+  } while (0)
+  if (nstep > 0) BCJR_WAVE_LOAD(0);
+  for (long long q = 0;; ++q) {
+    // store the boundary vector (normalised) and expectations of this segment
+    const long long sgb = seg_of(q);
+    const double sh = floor(wave_max(own ? v : -INFINITY));
+    if (own) {
+      (fwd ? lam0 : rho1)[sgb * M + l] = v - sh;
+      if constexpr (MOM) (fwd ? phi0 : psi1)[sgb * M + l] = mom;
+    }
+    if (l == 0) sc0[sgb * 2 + (fwd ? 0 : 1)] = sh;
+    if (q == nstep) break;
+    // stage this step's rows; start loading the next step's
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kWaveTile; ++u) {
+      const int f = l + 64 * u;
+      if (f < nv) {
+        const int e = 4 * f, i = e / M, j = e % M;
+        float* d = tq + i * RS + j;
+        d[0] = rq[u].x; d[1] = rq[u].y; d[2] = rq[u].z; d[3] = rq[u].w;
+        if constexpr (MOM) {
+          float* g = tf + i * RS + j;
+          g[0] = rf[u].x; g[1] = rf[u].y; g[2] = rf[u].z; g[3] = rf[u].w;
+        }
+      }
+    }
+    const double rsq = rs;
+    // fwd input a(i) = v(i) + rs(i); bwd input rho(j) = v(j)
+    const double a = own ? (fwd ? v + rsq : v) : -INFINITY;
+    const double m_in = wave_max(a);
+    if (own) {
+      vin[l] = (float)(a - m_in);
+      if constexpr (MOM) min_[l] = mom;
+    }
+    __syncthreads();
+    if (q + 1 < nstep) BCJR_WAVE_LOAD(q + 1);
+    if (own) {
+      // forward: column l of the rows (over i); backward: row l (over j)
+      const int base = fwd ? l : l * RS;
+      const int stride = fwd ? RS : 1;
+      // (the moment variant re-reads the LDS in the second pass, unrolled by 8 only: it
+      // already holds two prefetched tiles in registers)
+      float mx = -INFINITY, sm = 0.f, tm = 0.f;
+      if constexpr (!MOM) {
+        float x[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+          x[i] = vin[i] + tq[base + i * stride];
+          mx = fmaxf(mx, x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < M; ++i) sm += ex2(x[i] - mx);
+      } else {
+#pragma unroll 8
+        for (int i = 0; i < M; ++i) mx = fmaxf(mx, vin[i] + tq[base + i * stride]);
+#pragma unroll 8
+        for (int i = 0; i < M; ++i) {
+          const float e = ex2(vin[i] + tq[base + i * stride] - mx);
+          sm += e;
+          tm = __builtin_fmaf(e, min_[i] + tf[base + i * stride], tm);
+        }
+      }
+      v = (fwd ? m_in : rsq + m_in) + (double)mx + (double)lg2(sm);
+      if constexpr (MOM) mom = tm / sm;
+    }
+  }
+#undef BCJR_WAVE_LOAD
+}
+
 }  // namespace
 
 int launch_scan_bounds(const float* rows, const double* rscale, const float* frows, int64_t chains,
@@ -256,13 +379,27 @@ int launch_scan_bounds(const float* rows, const double* rscale, const float* fro
   if (chains <= 0) return 0;
   if (M < 4 || M > 1024 || (M & (M - 1))) return (int)hipErrorInvalidValue;
   const bool mom = frows != nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M <= 64) {
+#define BCJR_WAVE(M_)                                                                           \
+  if (M == M_) {                                                                                \
+    if (mom)                                                                                    \
+      hipLaunchKernelGGL((k_scan_wave<M_, true>), dim3((unsigned)chains, 2), dim3(64), 0, st,    \
+                         rows, rscale, frows, (long long)ptot, lam0, rho1, sc0, phi0, psi1);    \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_scan_wave<M_, false>), dim3((unsigned)chains, 2), dim3(64), 0, st,   \
+                         rows, rscale, frows, (long long)ptot, lam0, rho1, sc0, phi0, psi1);    \
+    return (int)hipGetLastError();                                                              \
+  }
+    BCJR_WAVE(4) BCJR_WAVE(8) BCJR_WAVE(16) BCJR_WAVE(32) BCJR_WAVE(64)
+#undef BCJR_WAVE
+  }
   // rows per staged tile: R * M <= 8192 floats (4096 with the moment tile beside it), so the
   // LDS stays under 64 KiB up to M = 1024; R >= 4 keeps a backward row within one wave
   const int tf = mom ? kTileFloats / 2 : kTileFloats;
   const int R = M * M <= tf ? M : tf / M;
   const size_t lds = (size_t)(2 * M + 4) * sizeof(double) + (size_t)3 * M * sizeof(float) +
                      (size_t)(mom ? 2 : 1) * R * (M + 4) * sizeof(float);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (mom)
     hipLaunchKernelGGL(k_scan_bounds<true>, dim3((unsigned)chains, 2), dim3(kScanBlock), lds, st,
                        rows, rscale, frows, (long long)ptot, M, R, lam0, rho1, sc0, phi0, psi1);
