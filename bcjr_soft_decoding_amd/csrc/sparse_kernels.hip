@@ -116,6 +116,8 @@ struct Cfg {
   // second barrier per step.
   static constexpr bool DB = 2 * BUF_BYTES <= 128 * 1024;
   static constexpr int NBUF = DB ? 2 : 1;
+  // chains of 1024 lanes run the rolled-loop kernels (k_sparse_fwd_wide)
+  static constexpr bool WIDE = LPS >= 1024;
 };
 
 // Cross-lane moves through DPP (no LDS round trip). CTRL: 0xB1 / 0x4E = quad_perm xor 1 / 2,
@@ -626,6 +628,253 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 }
 
 // ---------------------------------------------------------------------------------------------
+// Forward for chains of 1024 lanes (one 16-wave block per chain, so at most 128 registers per
+// lane). There the lane's blocks do not fit in registers together with their messages, codebook
+// values and intermediates, so the G blocks are visited in a rolled loop: a block's column
+// offsets are read from LDS when it is processed, its outputs go straight to the other message
+// buffer (one buffer per step parity), and the codebook values and history entries of the next
+// block are loaded while the current one is computed. The per-block arithmetic and the history
+// layout are those of k_sparse_fwd (mode 0).
+// ---------------------------------------------------------------------------------------------
+template <class C, bool CK>
+__global__ void __launch_bounds__(C::BLOCK)
+k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, long long B,
+                  long long L, Consts k, float* __restrict__ w_hat, float* __restrict__ log_z,
+                  double* __restrict__ saved_lz, float* __restrict__ saved_what,
+                  void* __restrict__ ws, size_t slot_bytes, long long units, long long seg_arg) {
+  using P = typename C::P;
+  using MT = typename C::MT;
+  constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
+  static_assert(C::SPB == 1 && C::BLOCK == LPS && C::DB, "one chain per block, two buffers");
+  __shared__ __attribute__((aligned(16))) MT msg[2][M];
+  __shared__ double red[2 * C::NWAVES * 4];
+  const int p = threadIdx.x;
+  CodebookLane<C, true> vsrc;
+  vsrc.init(cb, k.sc, p);
+
+  const long long seg = CK ? seg_arg : 0;
+  const long long ncp = seg ? (L + seg - 1) / seg : L;
+  const long long nh = seg ? ncp + seg : L;
+  char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
+  MT* __restrict__ hs = reinterpret_cast<MT*>(sb);
+  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * LPS * KG * 8);
+  auto hist = [&](long long e) { return hs + ((size_t)e * LPS + p) * KG; };
+  int rp = 0;
+
+  // units == B (one chain per unit), so every unit is a chain
+  for (long long b = blockIdx.x; b < units; b += gridDim.x) {
+    const float* __restrict__ wb = w + b * L;
+    __syncthreads();  // the previous chain is done with both buffers
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int a = 0; a < K; ++a) msg[0][p + g * LPS + a * NG] = (MT)0;
+    __syncthreads();
+
+    int cur = 0;    // buffer holding the current step's column values
+    MT sh = (MT)0;  // shift still to be subtracted from them
+    // the column offsets of step t (msg[cur] - sh) as history entry e
+    auto record = [&](long long e) {
+#pragma unroll 1
+      for (int g = 0; g < G; ++g) {
+        MT lc[K];
+#pragma unroll
+        for (int a = 0; a < K; ++a) lc[a] = msg[cur][p + g * LPS + a * NG] - sh;
+        store_vec<K>(hist(e) + g * K, lc);
+      }
+    };
+    // One forward step: offsets of step t -> raw outputs of step t + 1 in msg[cur ^ 1]; records
+    // the offsets as history entry e (e >= 0) and returns the outputs' chain-wide maximum.
+    auto fstep = [&](long long t, long long e) -> MT {
+      const float u = k.sc * wb[t];
+      const MT* __restrict__ src = msg[cur];
+      MT* __restrict__ dst = msg[cur ^ 1];
+      MT mx = (MT)-INFINITY;
+      float Vn[K][K];
+      vsrc.get(0, Vn);
+#pragma unroll 1
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K];
+#pragma unroll
+        for (int r = 0; r < K; ++r)
+#pragma unroll
+          for (int a = 0; a < K; ++a) Vg[r][a] = Vn[r][a];
+        if (g + 1 < G) vsrc.get(g + 1, Vn);
+        MT lc[K];
+#pragma unroll
+        for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
+        if (e >= 0) store_vec<K>(hist(e) + g * K, lc);
+        MT out[K];
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          MT x[K];
+          MT m = (MT)-INFINITY;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            x[a] = emit<P>(u, Vg[r][a], lc[a], k.kap);
+            m = tmax(m, x[a]);
+          }
+          float s = ex2((float)(x[0] - m));
+#pragma unroll
+          for (int a = 1; a < K; ++a) s += ex2((float)(x[a] - m));
+          out[r] = m + (MT)lg2(s);
+          mx = tmax(mx, out[r]);
+        }
+        store_vec<K>(dst + K * (p + g * LPS), out);
+      }
+      MT v1[1] = {mx};
+      chain_reduce<C, 1, 1u>(v1, red, rp);
+      return v1[0];
+    };
+
+    // ---- phase A: forward messages, t = 0 .. L-1 ---------------------------------------------
+    double N = 0.0, lz2 = 0.0;
+    for (long long t = 0;; ++t) {
+      if (p == 0) ns[t] = N;
+      const long long e = seg == 0 ? t : (t % seg == 0 ? t / seg : -1);
+      const MT mx = fstep(t, e);
+      if (t == L - 1) {  // log2 Z = N + LSE of the last outputs (this lane's own rows)
+        float s2 = 0.f;
+#pragma unroll 1
+        for (int g = 0; g < G; ++g) {
+          MT o[K];
+          load_vec<K>(msg[cur ^ 1] + K * (p + g * LPS), o);
+#pragma unroll
+          for (int r = 0; r < K; ++r) s2 += ex2((float)(o[r] - mx));
+        }
+        float v2[1] = {s2};
+        chain_reduce<C, 1, 0u>(v2, red, rp);
+        lz2 = N + ((double)mx + (double)lg2(v2[0]));
+        break;
+      }
+      sh = floor(mx);
+      N += (double)sh;
+      cur ^= 1;
+    }
+
+    // ---- phase B: backward messages, posterior and soft codeword, t = L-1 .. 0 ---------------
+    // A lane reads only its own rows K*(p + g*LPS) + r of the current buffer (rho at step t,
+    // raw, minus shp) and writes its columns of the other.
+    __syncthreads();  // phase-A history (incl. lane 0's N) visible; buffers free
+    int rb = 0;
+    MT shp = (MT)0;
+    double Np = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      MT z[K];
+#pragma unroll
+      for (int r = 0; r < K; ++r) z[r] = (MT)0;
+      store_vec<K>(msg[0] + K * (p + g * LPS), z);
+    }
+    const long long nseg = seg ? ncp : 1;
+    for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
+      const long long t0 = seg ? sgi * seg : 0;
+      const long long t1 = seg ? (t0 + seg < L ? t0 + seg : L) : L;
+      if (CK) {
+        // replay the segment's forward offsets from its checkpoint through both buffers,
+        // keeping this lane's rows of the backward buffer in registers meanwhile
+        MT keep[G][K];
+#pragma unroll
+        for (int g = 0; g < G; ++g) load_vec<K>(msg[rb] + K * (p + g * LPS), keep[g]);
+        __syncthreads();
+        MT c0[KG];
+        load_vec<KG>(hist(sgi), c0);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int a = 0; a < K; ++a) msg[0][p + g * LPS + a * NG] = c0[g * K + a];
+        __syncthreads();
+        cur = 0;
+        sh = (MT)0;
+        for (long long t = t0; t + 1 < t1; ++t) {
+          const MT mx = fstep(t, ncp + (t - t0));
+          sh = floor(mx);
+          cur ^= 1;
+        }
+        record(ncp + (t1 - 1 - t0));
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < G; ++g) store_vec<K>(msg[rb] + K * (p + g * LPS), keep[g]);
+      }
+      auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
+      float Vn[K][K];
+      vsrc.get(0, Vn);
+      MT ln[K];
+      load_vec<K>(hist(entry(t1 - 1)), ln);
+      for (long long t = t1 - 1; t >= t0; --t) {
+        const double Nt = ns[t];
+        const float u = k.sc * wb[t];
+        const MT LZ = (MT)((lz2 - Nt) - Np);
+        const MT* __restrict__ src = msg[rb];
+        MT* __restrict__ dst = msg[rb ^ 1];
+        float num = 0.f, den = 0.f;
+        MT mx = (MT)-INFINITY;
+#pragma unroll 1
+        for (int g = 0; g < G; ++g) {
+          float Vg[K][K];
+          MT lcur[K];
+#pragma unroll
+          for (int r = 0; r < K; ++r)
+#pragma unroll
+            for (int a = 0; a < K; ++a) Vg[r][a] = Vn[r][a];
+#pragma unroll
+          for (int a = 0; a < K; ++a) lcur[a] = ln[a];
+          // next block's codebook values and history entry (block 0 of step t - 1 after the last)
+          vsrc.get(g + 1 < G ? g + 1 : 0, Vn);
+          if (g + 1 < G)
+            load_vec<K>(hist(entry(t)) + (g + 1) * K, ln);
+          else if (t > t0)
+            load_vec<K>(hist(entry(t - 1)), ln);
+          MT rr[K];
+          load_vec<K>(src + K * (p + g * LPS), rr);
+#pragma unroll
+          for (int r = 0; r < K; ++r) rr[r] -= shp;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            MT y[K];
+            MT m = (MT)-INFINITY;
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              y[r] = emit<P>(u, Vg[r][a], rr[r], k.kap);
+              m = tmax(m, y[r]);
+            }
+            float e0 = ex2((float)(y[0] - m));
+            float cs = e0, cw = Vg[0][a] * e0;
+#pragma unroll
+            for (int r = 1; r < K; ++r) {
+              const float e = ex2((float)(y[r] - m));
+              cs += e;
+              cw = __builtin_fmaf(Vg[r][a], e, cw);
+            }
+            const MT ro = m + (MT)lg2(cs);
+            mx = tmax(mx, ro);
+            const float f = ex2((float)((m + lcur[a]) - LZ));
+            num = __builtin_fmaf(f, cw, num);
+            den = __builtin_fmaf(f, cs, den);
+            if (t > 0) dst[p + g * LPS + a * NG] = ro;
+          }
+        }
+        MT v3[3] = {(MT)num, (MT)den, mx};
+        chain_reduce<C, 3, 4u>(v3, red, rp);
+        if (p == 0) {
+          const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
+          w_hat[b * L + t] = wh;
+          saved_what[b * L + t] = wh;
+        }
+        if (t == 0) break;
+        shp = floor(v3[2]);
+        Np += (double)shp;
+        rb ^= 1;
+      }
+    }
+    if (p == 0) {
+      log_z[b] = (float)(lz2 * (double)kLn2);
+      saved_lz[b] = lz2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Backward: gradient of F = sum_t g_t w_hat_t + h log Z w.r.t. w and the codebook.
 // With the posterior written as a Markov chain, E[F | s_t = s] = Fwd_t(s) + g_t c(s) + Bwd_t(s)
 // where the conditional expectations obey the same butterfly factorisation as the messages:
@@ -1099,19 +1348,35 @@ int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
   double* slz = reinterpret_cast<double*>(saved);
   float* swh = saved + saved_what_offset(B);
-  const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_fwd<C, true>)
-                          : reinterpret_cast<const void*>(&k_sparse_fwd<C, false>);
-  const int grid = resident_grid(kern, C::BLOCK, g.slots);
-  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
-  if (ckpt)
-    hipLaunchKernelGGL((k_sparse_fwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
-                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg,
-                       SegArgs{});
-  else
-    hipLaunchKernelGGL((k_sparse_fwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
-                       B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg,
-                       SegArgs{});
-  return (int)hipGetLastError();
+  if constexpr (C::WIDE) {
+    const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_fwd_wide<C, true>)
+                            : reinterpret_cast<const void*>(&k_sparse_fwd_wide<C, false>);
+    const int grid = resident_grid(kern, C::BLOCK, g.slots);
+    if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+    if (ckpt)
+      hipLaunchKernelGGL((k_sparse_fwd_wide<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st,
+                         cb, w, B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units,
+                         seg);
+    else
+      hipLaunchKernelGGL((k_sparse_fwd_wide<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0,
+                         st, cb, w, B, L, kc, w_hat, log_z, slz, swh, ws, slot,
+                         (long long)g.units, seg);
+    return (int)hipGetLastError();
+  } else {
+    const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_fwd<C, true>)
+                            : reinterpret_cast<const void*>(&k_sparse_fwd<C, false>);
+    const int grid = resident_grid(kern, C::BLOCK, g.slots);
+    if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+    if (ckpt)
+      hipLaunchKernelGGL((k_sparse_fwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb,
+                         w, B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg,
+                         SegArgs{});
+    else
+      hipLaunchKernelGGL((k_sparse_fwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb,
+                         w, B, L, kc, w_hat, log_z, slz, swh, ws, slot, (long long)g.units, seg,
+                         SegArgs{});
+    return (int)hipGetLastError();
+  }
 }
 
 template <int n, int k, class P>
