@@ -1293,6 +1293,394 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 }
 
 // out[s] = sum over slots of the partials, in slot order (deterministic); with no slots, 0.
+// ---------------------------------------------------------------------------------------------
+// Backward for chains of 1024 lanes. Each message array of a chain (lam / rho and Phi / Psi)
+// fills LDS with a single buffer, so a step reads its inputs from LDS while it computes, keeps
+// its outputs in registers until every lane has read (the chain reduction's barrier), then
+// writes them. The codebook-gradient accumulators (one per state) do not fit in registers next
+// to that: they live in the slot's partial row in global memory, which the reduction kernel
+// sums anyway, and each block column's four are read, updated and written back once per step.
+// With checkpoints, the segment replay runs through the same buffers; the lane's backward rows
+// are parked meanwhile in the history entry of the checkpoint after the segment's, which the
+// backward sweep no longer needs. Per-state arithmetic as in k_sparse_bwd (mode 0).
+// ---------------------------------------------------------------------------------------------
+// A lane offset made opaque to the optimiser at each use, so that addresses built from it are
+// formed where they are used instead of being hoisted out of the step loops as 64-bit address
+// registers (one pair per block column, which would not fit next to the messages).
+__device__ __forceinline__ unsigned opaque(unsigned x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// Pins a value's computation at this point. The step outputs are stored only after the chain
+// reduction's barrier; without the pin the compiler sinks their arithmetic past it and keeps
+// every intermediate of the step alive across the reduction.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+template <class C, bool CK>
+__global__ void __launch_bounds__(C::BLOCK)
+k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, long long B,
+                  long long L, Consts k, const double* __restrict__ saved_lz,
+                  const float* __restrict__ saved_what, const float* __restrict__ gup,
+                  const float* __restrict__ hup, float* __restrict__ grad_w,
+                  float* __restrict__ partial, void* __restrict__ ws, size_t slot_bytes,
+                  long long units, long long seg_arg) {
+  using P = typename C::P;
+  using MT = typename C::MT;
+  constexpr int K = C::K, G = C::G, LPS = C::LPS, NG = C::NG, M = C::M, KG = C::KG;
+  static_assert(C::SPB == 1 && C::BLOCK == LPS, "one chain per block");
+  __shared__ __attribute__((aligned(16))) MT msgl[M];
+  __shared__ __attribute__((aligned(16))) float msgp[M];
+  __shared__ double red[2 * C::NWAVES * 4];
+  const int p = threadIdx.x;
+  const float k2 = 2.0f * k.inv_t * k.csc;  // (2/T)(w - c) = k2 * (u - v)
+  // State K*(p + g*LPS) + r + a*M (block g, row r, column a) of the codebook and of the slot's
+  // accumulators: a block-uniform base plus the 32-bit lane offset lo4 = K*p, so that the
+  // per-column addresses stay in scalar registers.
+  const unsigned lo4 = K * p;
+  float* __restrict__ accs = partial + (size_t)blockIdx.x * C::S;
+  auto col = [](int g, int a) { return g * K * LPS + a * M; };
+  auto vcol = [&](int g, int a, float (&v)[K]) {  // codebook values of one block column
+    float tmp[K];
+    const float* __restrict__ ub = cb + col(g, a);
+    load_vec<K>(ub + opaque(lo4), tmp);
+#pragma unroll
+    for (int r = 0; r < K; ++r) v[r] = k.sc * tmp[r];
+  };
+  auto vblock = [&](int g, float (&v)[K][K]) {  // the whole block, v[r][a]
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      float c4[K];
+      vcol(g, a, c4);
+#pragma unroll
+      for (int r = 0; r < K; ++r) v[r][a] = c4[r];
+    }
+  };
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      float z[K];
+#pragma unroll
+      for (int r = 0; r < K; ++r) z[r] = 0.f;
+      float* __restrict__ ub = accs + col(g, a);
+      store_vec<K>(ub + opaque(lo4), z);
+    }
+
+  const long long seg = CK ? seg_arg : 0;
+  const long long ncp = seg ? (L + seg - 1) / seg : L;
+  const long long nh = seg ? ncp + seg : L;
+  char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
+  MT* __restrict__ hl = reinterpret_cast<MT*>(sb);
+  float* __restrict__ hp = reinterpret_cast<float*>(sb + (size_t)nh * LPS * KG * 8);
+  double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * LPS * KG * 12);
+  // history entry e of this lane: block-uniform base + 32-bit lane offset lh
+  const unsigned lh = p * KG;
+  auto histl = [&](long long e) { return hl + (size_t)e * LPS * KG; };
+  auto histp = [&](long long e) { return hp + (size_t)e * LPS * KG; };
+  int rp = 0;
+
+  for (long long b = blockIdx.x; b < units; b += gridDim.x) {
+    const float* __restrict__ wb = w + b * L;
+    const float* __restrict__ gb = gup + b * L;
+    const float* __restrict__ whb = saved_what + b * L;
+    const float h = hup != nullptr ? hup[b] : 0.f;
+    const double lz2 = saved_lz[b];
+
+    __syncthreads();  // the previous chain is done with the buffers
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        msgl[p + g * LPS + a * NG] = (MT)0;
+        msgp[p + g * LPS + a * NG] = 0.f;
+      }
+    __syncthreads();
+
+    MT sh = (MT)0;  // shift still to be subtracted from the column values in msgl
+    // the column offsets (lam - sh, Phi) of the current step as history entry e
+    auto record = [&](long long e) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        MT lc[K];
+        float pc[K];
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          lc[a] = msgl[p + g * LPS + a * NG] - sh;
+          pc[a] = msgp[p + g * LPS + a * NG];
+        }
+        store_vec<K>(histl(e) + g * K + opaque(lh), lc);
+        store_vec<K>(histp(e) + g * K + opaque(lh), pc);
+      }
+    };
+    // One forward step (lam, Phi) of step t -> raw rows of step t + 1, written over the buffer
+    // once every lane has read; records the inputs as entry e (e >= 0); returns the outputs'
+    // chain-wide maximum.
+    auto advance = [&](long long t, long long e) -> MT {
+      const float u = k.sc * wb[t];
+      const float gtp = gb[t] * k.csc;   // g_t c(s) = gtp * v(s)
+      const float gwh = gb[t] * whb[t];  // g_t w_hat_t
+      if (e >= 0) record(e);  // (before the arithmetic, which then has no branch in it)
+      MT lo[G][K];
+      float po[G][K];
+      MT mx = (MT)-INFINITY;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K];
+        vblock(g, Vg);
+        MT lc[K];
+        float pcc[K];
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          lc[a] = msgl[p + g * LPS + a * NG] - sh;
+          pcc[a] = msgp[p + g * LPS + a * NG] - gwh;
+        }
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          MT x[K];
+          MT m = (MT)-INFINITY;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            x[a] = emit<P>(u, Vg[r][a], lc[a], k.kap);
+            m = tmax(m, x[a]);
+          }
+          float e0 = ex2((float)(x[0] - m));
+          float s = e0, ph = e0 * __builtin_fmaf(gtp, Vg[r][0], pcc[0]);
+#pragma unroll
+          for (int a = 1; a < K; ++a) {
+            const float ea = ex2((float)(x[a] - m));
+            s += ea;
+            ph = __builtin_fmaf(ea, __builtin_fmaf(gtp, Vg[r][a], pcc[a]), ph);
+          }
+          lo[g][r] = m + (MT)lg2(s);
+          po[g][r] = ph * rcp_nr(s);
+          pin(lo[g][r]);
+          pin(po[g][r]);
+          mx = tmax(mx, lo[g][r]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      MT v1[1] = {mx};
+      chain_reduce<C, 1, 1u>(v1, red, rp);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        store_vec<K>(msgl + K * (p + g * LPS), lo[g]);
+        store_vec<K>(msgp + K * (p + g * LPS), po[g]);
+      }
+      __syncthreads();
+      return v1[0];
+    };
+
+    // ---- phase A: lam and Phi, t = 0 .. L-1, plus one step to t = L -------------------------
+    double N = 0.0;
+    MT shL = (MT)0;
+    for (long long t = 0; t < L; ++t) {
+      if (p == 0) ns[t] = N;
+      const long long e = seg == 0 ? t : (t % seg == 0 ? t / seg : -1);
+      const MT s = floor(advance(t, e));
+      if (t == L - 1) {
+        shL = s;
+        break;
+      }
+      sh = s;
+      N += (double)s;
+    }
+    // posterior weights of butterfly j at t = L (rho = 0 at the free end): the weighted mean of
+    // Phi_L(j) is the mean xbar of the centred expectation at the last step
+    float xbar;
+    {
+      MT ymx = (MT)-INFINITY;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        MT y[K];
+        load_vec<K>(msgl + K * (p + g * LPS), y);
+#pragma unroll
+        for (int r = 0; r < K; ++r) ymx = tmax(ymx, y[r] - shL);
+      }
+      MT v1[1] = {ymx};
+      chain_reduce<C, 1, 1u>(v1, red, rp);
+      float s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        MT y[K];
+        float pm[K];
+        load_vec<K>(msgl + K * (p + g * LPS), y);
+        load_vec<K>(msgp + K * (p + g * LPS), pm);
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          const float e = ex2((float)((y[r] - shL) - v1[0]));
+          s2 += e;
+          s3 = __builtin_fmaf(e, pm[r], s3);
+        }
+      }
+      float v2[2] = {s2, s3};
+      chain_reduce<C, 2, 0u>(v2, red, rp);
+      xbar = v2[1] / v2[0];
+    }
+
+    // ---- phase B: rho and Psi, posterior, D, gradients, t = L-1 .. 0 ------------------------
+    // A lane reads its own rows K*(p + g*LPS) + r (rho raw minus shp, Psi) and writes columns.
+    MT shp = (MT)0;
+    double Np = 0.0;
+    auto set_rows = [&](const MT* lsrc, const float* psrc) {  // own rows from history-shaped data
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        MT l4[K];
+        float p4[K];
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          l4[r] = lsrc ? lsrc[g * K + r] : (MT)0;
+          p4[r] = psrc ? psrc[g * K + r] : 0.f;
+        }
+        store_vec<K>(msgl + K * (p + g * LPS), l4);
+        store_vec<K>(msgp + K * (p + g * LPS), p4);
+      }
+    };
+    set_rows(nullptr, nullptr);
+    const long long nseg = seg ? ncp : 1;
+    for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
+      const long long t0 = seg ? sgi * seg : 0;
+      const long long t1 = seg ? (t0 + seg < L ? t0 + seg : L) : L;
+      if (CK) {
+        const bool park = sgi + 1 < nseg;
+        if (park) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            MT l4[K];
+            float p4[K];
+            load_vec<K>(msgl + K * (p + g * LPS), l4);
+            load_vec<K>(msgp + K * (p + g * LPS), p4);
+            store_vec<K>(histl(sgi + 1) + g * K + opaque(lh), l4);
+            store_vec<K>(histp(sgi + 1) + g * K + opaque(lh), p4);
+          }
+        }
+        __syncthreads();
+        {
+          MT c0[KG];
+          float q0[KG];
+          load_vec<KG>(histl(sgi) + opaque(lh), c0);
+          load_vec<KG>(histp(sgi) + opaque(lh), q0);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int a = 0; a < K; ++a) {
+              msgl[p + g * LPS + a * NG] = c0[g * K + a];
+              msgp[p + g * LPS + a * NG] = q0[g * K + a];
+            }
+        }
+        __syncthreads();
+        sh = (MT)0;
+        for (long long t = t0; t + 1 < t1; ++t) sh = floor(advance(t, ncp + (t - t0)));
+        record(ncp + (t1 - 1 - t0));
+        __syncthreads();
+        if (park) {
+          MT c1[KG];
+          float q1[KG];
+          load_vec<KG>(histl(sgi + 1) + opaque(lh), c1);
+          load_vec<KG>(histp(sgi + 1) + opaque(lh), q1);
+          set_rows(c1, q1);
+        } else {
+          set_rows(nullptr, nullptr);
+        }
+      }
+      auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
+      for (long long t = t1 - 1; t >= t0; --t) {
+        const double Nt = ns[t];
+        const float u = k.sc * wb[t];
+        const float gt = gb[t];
+        const float gtp = gt * k.csc;
+        const float gwh = gt * whb[t];
+        const MT LZ = (MT)((lz2 - Nt) - Np);
+        // E_t(s) = gamma (X - xbar + h) with X = Phi + g (c - w_hat) + Psi; xs sums it over the
+        // states, so xs - h is the part of the mean of X that xbar did not remove
+        const float hx = h - xbar;
+        float gw = 0.f, xs = 0.f;
+        MT mx = (MT)-INFINITY;
+        MT ro[G][K];
+        float qo[G][K];
+        const MT* __restrict__ hlt = histl(entry(t));
+        const float* __restrict__ hpt = histp(entry(t));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          MT lcur[K], rr[K];
+          float pcur[K], qrc[K];
+          load_vec<K>(hlt + g * K + opaque(lh), lcur);
+          load_vec<K>(hpt + g * K + opaque(lh), pcur);
+          load_vec<K>(msgl + K * (p + g * LPS), rr);
+          load_vec<K>(msgp + K * (p + g * LPS), qrc);
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            rr[r] -= shp;
+            qrc[r] -= gwh;  // Psi_t - g_t w_hat_t at the row offsets
+          }
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            float V[K], ac[K];
+            vcol(g, a, V);
+            float* __restrict__ ua = accs + col(g, a);
+            load_vec<K>(ua + opaque(lo4), ac);
+            MT y[K];
+            float dd[K];
+            MT m = (MT)-INFINITY;
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              dd[r] = u - V[r];
+              y[r] = emit<P>(u, V[r], rr[r], k.kap);
+              m = tmax(m, y[r]);
+            }
+            float e[K], t2[K];
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              e[r] = ex2((float)(y[r] - m));
+              t2[r] = __builtin_fmaf(gtp, V[r], qrc[r]);
+            }
+            float cs = e[0], ps = e[0] * t2[0];
+#pragma unroll
+            for (int r = 1; r < K; ++r) {
+              cs += e[r];
+              ps = __builtin_fmaf(e[r], t2[r], ps);
+            }
+            ro[g][a] = m + (MT)lg2(cs);
+            qo[g][a] = ps * rcp_nr(cs);
+            pin(ro[g][a]);
+            pin(qo[g][a]);
+            mx = tmax(mx, ro[g][a]);
+            const float f = ex2((float)((m + lcur[a]) - LZ));
+            const float pa = pcur[a] + hx;
+            xs = __builtin_fmaf(f, __builtin_fmaf(pa, cs, ps), xs);
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              const float gm = e[r] * f;
+              const float eh = gm * (t2[r] + pa);
+              gw = __builtin_fmaf(V[r], eh, gw);
+              ac[r] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, ac[r]));
+            }
+            store_vec<K>(ua + opaque(lo4), ac);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        MT v2[3] = {(MT)gw, mx, (MT)xs};
+        chain_reduce<C, 3, 2u>(v2, red, rp);
+        xbar += (float)v2[2] - h;
+        if (p == 0) grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+        if (t == 0) break;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            msgl[p + g * LPS + a * NG] = ro[g][a];
+            msgp[p + g * LPS + a * NG] = qo[g][a];
+          }
+        __syncthreads();
+        shp = floor(v2[1]);
+        Np += (double)shp;
+      }
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256)
 k_reduce_slots(const float* __restrict__ partial, long long slots, long long count,
                float* __restrict__ out) {
@@ -1392,18 +1780,34 @@ int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + slot * (size_t)g.slots);
   const double* slz = reinterpret_cast<const double*>(saved);
   const float* swh = saved + saved_what_offset(B);
-  const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_bwd<C, true>)
-                          : reinterpret_cast<const void*>(&k_sparse_bwd<C, false>);
-  const int grid = resident_grid(kern, C::BLOCK, g.slots);
-  if (grid <= 0) return (int)hipErrorInvalidConfiguration;
-  if (ckpt)
-    hipLaunchKernelGGL((k_sparse_bwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
-                       B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units,
-                       seg, SegArgs{});
-  else
-    hipLaunchKernelGGL((k_sparse_bwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb, w,
-                       B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot, (long long)g.units,
-                       seg, SegArgs{});
+  int grid;
+  if constexpr (C::WIDE) {
+    const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_bwd_wide<C, true>)
+                            : reinterpret_cast<const void*>(&k_sparse_bwd_wide<C, false>);
+    grid = resident_grid(kern, C::BLOCK, g.slots);
+    if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+    if (ckpt)
+      hipLaunchKernelGGL((k_sparse_bwd_wide<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st,
+                         cb, w, B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot,
+                         (long long)g.units, seg);
+    else
+      hipLaunchKernelGGL((k_sparse_bwd_wide<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0,
+                         st, cb, w, B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot,
+                         (long long)g.units, seg);
+  } else {
+    const void* kern = ckpt ? reinterpret_cast<const void*>(&k_sparse_bwd<C, true>)
+                            : reinterpret_cast<const void*>(&k_sparse_bwd<C, false>);
+    grid = resident_grid(kern, C::BLOCK, g.slots);
+    if (grid <= 0) return (int)hipErrorInvalidConfiguration;
+    if (ckpt)
+      hipLaunchKernelGGL((k_sparse_bwd<C, true>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb,
+                         w, B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot,
+                         (long long)g.units, seg, SegArgs{});
+    else
+      hipLaunchKernelGGL((k_sparse_bwd<C, false>), dim3((unsigned)grid), dim3(C::BLOCK), 0, st, cb,
+                         w, B, L, kc, slz, swh, gup, hup, grad_w, partial, ws, slot,
+                         (long long)g.units, seg, SegArgs{});
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((C::S + 255) / 256)), dim3(256), 0, st, partial,
