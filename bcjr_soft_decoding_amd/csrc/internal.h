@@ -66,9 +66,14 @@ inline size_t sparse_fwd_slot_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
   return round256((size_t)sparse_hist_entries(L, ckpt) * g.BLOCK * (g.K * g.G) * 8 +
                   (size_t)L * g.SPB * 8);
 }
+// Chains of 1024 lanes (k_sparse_bwd_wide) also record their backward rows per history entry
+// ([H][BLOCK][K*G], 8-byte + fp32 entries, after the shift prefix rounded to 256 bytes) and, per
+// step, the posterior normaliser (double) and the centring mean (fp32).
 inline size_t sparse_bwd_slot_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
-  return round256((size_t)sparse_hist_entries(L, ckpt) * g.BLOCK * (g.K * g.G) * 12 +
-                  (size_t)L * g.SPB * 8);
+  const size_t hist = (size_t)sparse_hist_entries(L, ckpt) * g.BLOCK * (g.K * g.G) * 12;
+  if (g.LPS >= kMaxLanesPerChain)
+    return round256(hist + round256((size_t)L * 8) + hist + (size_t)L * 12);
+  return round256(hist + (size_t)L * g.SPB * 8);
 }
 // Forward / backward workspace for the fp32-message geometry g: enough for either message
 // precision (the fp64-message kernels run with the kFwdP / kBwdP geometry of the same n, k, B).

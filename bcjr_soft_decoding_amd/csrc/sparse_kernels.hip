@@ -658,7 +658,9 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
   MT* __restrict__ hs = reinterpret_cast<MT*>(sb);
   double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * LPS * KG * 8);
-  auto hist = [&](long long e) { return hs + ((size_t)e * LPS + p) * KG; };
+  // history entries are block-major, [H][G][LPS][K]: block g of this lane in entry e is at
+  // hist(e) + g*LPS*K
+  auto hist = [&](long long e) { return hs + (size_t)e * LPS * KG + K * p; };
   int rp = 0;
 
   // units == B (one chain per unit), so every unit is a chain
@@ -680,7 +682,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         MT lc[K];
 #pragma unroll
         for (int a = 0; a < K; ++a) lc[a] = msg[cur][p + g * LPS + a * NG] - sh;
-        store_vec<K>(hist(e) + g * K, lc);
+        store_vec<K>(hist(e) + g * (LPS * K), lc);
       }
     };
     // One forward step: offsets of step t -> raw outputs of step t + 1 in msg[cur ^ 1]; records
@@ -703,7 +705,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         MT lc[K];
 #pragma unroll
         for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
-        if (e >= 0) store_vec<K>(hist(e) + g * K, lc);
+        if (e >= 0) store_vec<K>(hist(e) + g * (LPS * K), lc);
         MT out[K];
 #pragma unroll
         for (int r = 0; r < K; ++r) {
@@ -778,7 +780,8 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         for (int g = 0; g < G; ++g) load_vec<K>(msg[rb] + K * (p + g * LPS), keep[g]);
         __syncthreads();
         MT c0[KG];
-        load_vec<KG>(hist(sgi), c0);
+#pragma unroll
+        for (int g = 0; g < G; ++g) load_vec<K>(hist(sgi) + g * (LPS * K), c0 + g * K);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -822,7 +825,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           // next block's codebook values and history entry (block 0 of step t - 1 after the last)
           vsrc.get(g + 1 < G ? g + 1 : 0, Vn);
           if (g + 1 < G)
-            load_vec<K>(hist(entry(t)) + (g + 1) * K, ln);
+            load_vec<K>(hist(entry(t)) + (g + 1) * (LPS * K), ln);
           else if (t > t0)
             load_vec<K>(hist(entry(t - 1)), ln);
           MT rr[K];
@@ -1294,15 +1297,21 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 
 // out[s] = sum over slots of the partials, in slot order (deterministic); with no slots, 0.
 // ---------------------------------------------------------------------------------------------
+// ---------------------------------------------------------------------------------------------
 // Backward for chains of 1024 lanes. Each message array of a chain (lam / rho and Phi / Psi)
-// fills LDS with a single buffer, so a step reads its inputs from LDS while it computes, keeps
-// its outputs in registers until every lane has read (the chain reduction's barrier), then
-// writes them. The codebook-gradient accumulators (one per state) do not fit in registers next
-// to that: they live in the slot's partial row in global memory, which the reduction kernel
-// sums anyway, and each block column's four are read, updated and written back once per step.
-// With checkpoints, the segment replay runs through the same buffers; the lane's backward rows
-// are parked meanwhile in the history entry of the checkpoint after the segment's, which the
-// backward sweep no longer needs. Per-state arithmetic as in k_sparse_bwd (mode 0).
+// fills LDS with a single buffer, so a recursion step reads its inputs from LDS while it
+// computes, keeps its outputs in registers until every lane has read (the chain reduction's
+// barrier), then writes them. The per-state codebook-gradient sums (64 per lane) do not fit in
+// registers next to that, so they get a phase of their own:
+//   phase A: lam and Phi forward, recording the lane's column offsets per step (as k_sparse_bwd);
+//   phase B: rho and Psi backward with the posterior-weighted sums that give grad_w and the
+//            centring mean, recording the lane's row offsets and the per-step normaliser;
+//   phase C: block by block, the lane's 16 codebook-gradient sums over the steps, from the two
+//            recorded histories; the block's codebook values stay in registers for the pass and
+//            the sums are added into the slot's partial row once per pass.
+// With checkpoints, phases B and C run segment by segment after each segment's replay; the
+// lane's backward rows are parked meanwhile in the history entry of the checkpoint after the
+// segment's, which the backward sweep no longer needs.
 // ---------------------------------------------------------------------------------------------
 // A lane offset made opaque to the optimiser at each use, so that addresses built from it are
 // formed where they are used instead of being hoisted out of the step loops as 64-bit address
@@ -1376,10 +1385,20 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   MT* __restrict__ hl = reinterpret_cast<MT*>(sb);
   float* __restrict__ hp = reinterpret_cast<float*>(sb + (size_t)nh * LPS * KG * 8);
   double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * LPS * KG * 12);
-  // history entry e of this lane: block-uniform base + 32-bit lane offset lh
-  const unsigned lh = p * KG;
+  // backward rows: rho (8-byte entries) and Psi [H][LPS][KG], then per step the posterior
+  // normaliser LZ (double) and the centring mean xbar used at that step (fp32)
+  char* sr = sb + (size_t)nh * LPS * KG * 12 + (((size_t)L * 8 + 255) & ~(size_t)255);
+  MT* __restrict__ hr = reinterpret_cast<MT*>(sr);
+  float* __restrict__ hq = reinterpret_cast<float*>(sr + (size_t)nh * LPS * KG * 8);
+  double* __restrict__ lzt = reinterpret_cast<double*>(sr + (size_t)nh * LPS * KG * 12);
+  float* __restrict__ xbt = reinterpret_cast<float*>(lzt + L);
+  // History entries are block-major, [H][G][LPS][K]: block g of this lane in entry e is at
+  // the block-uniform base histX(e) + g*LPS*K plus the 32-bit lane offset lh = K*p.
+  const unsigned lh = K * p;
   auto histl = [&](long long e) { return hl + (size_t)e * LPS * KG; };
   auto histp = [&](long long e) { return hp + (size_t)e * LPS * KG; };
+  auto histr = [&](long long e) { return hr + (size_t)e * LPS * KG; };
+  auto histq = [&](long long e) { return hq + (size_t)e * LPS * KG; };
   int rp = 0;
 
   for (long long b = blockIdx.x; b < units; b += gridDim.x) {
@@ -1411,8 +1430,8 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           lc[a] = msgl[p + g * LPS + a * NG] - sh;
           pc[a] = msgp[p + g * LPS + a * NG];
         }
-        store_vec<K>(histl(e) + g * K + opaque(lh), lc);
-        store_vec<K>(histp(e) + g * K + opaque(lh), pc);
+        store_vec<K>(histl(e) + g * (LPS * K) + opaque(lh), lc);
+        store_vec<K>(histp(e) + g * (LPS * K) + opaque(lh), pc);
       }
     };
     // One forward step (lam, Phi) of step t -> raw rows of step t + 1, written over the buffer
@@ -1552,16 +1571,19 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             float p4[K];
             load_vec<K>(msgl + K * (p + g * LPS), l4);
             load_vec<K>(msgp + K * (p + g * LPS), p4);
-            store_vec<K>(histl(sgi + 1) + g * K + opaque(lh), l4);
-            store_vec<K>(histp(sgi + 1) + g * K + opaque(lh), p4);
+            store_vec<K>(histl(sgi + 1) + g * (LPS * K) + opaque(lh), l4);
+            store_vec<K>(histp(sgi + 1) + g * (LPS * K) + opaque(lh), p4);
           }
         }
         __syncthreads();
         {
           MT c0[KG];
           float q0[KG];
-          load_vec<KG>(histl(sgi) + opaque(lh), c0);
-          load_vec<KG>(histp(sgi) + opaque(lh), q0);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            load_vec<K>(histl(sgi) + g * (LPS * K) + opaque(lh), c0 + g * K);
+            load_vec<K>(histp(sgi) + g * (LPS * K) + opaque(lh), q0 + g * K);
+          }
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -1578,8 +1600,11 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         if (park) {
           MT c1[KG];
           float q1[KG];
-          load_vec<KG>(histl(sgi + 1) + opaque(lh), c1);
-          load_vec<KG>(histp(sgi + 1) + opaque(lh), q1);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            load_vec<K>(histl(sgi + 1) + g * (LPS * K) + opaque(lh), c1 + g * K);
+            load_vec<K>(histp(sgi + 1) + g * (LPS * K) + opaque(lh), q1 + g * K);
+          }
           set_rows(c1, q1);
         } else {
           set_rows(nullptr, nullptr);
@@ -1596,51 +1621,52 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         // E_t(s) = gamma (X - xbar + h) with X = Phi + g (c - w_hat) + Psi; xs sums it over the
         // states, so xs - h is the part of the mean of X that xbar did not remove
         const float hx = h - xbar;
+        if (p == 0) {
+          lzt[t] = (double)LZ;
+          xbt[t] = xbar;
+        }
+        const long long e = entry(t);
         float gw = 0.f, xs = 0.f;
         MT mx = (MT)-INFINITY;
         MT ro[G][K];
         float qo[G][K];
-        const MT* __restrict__ hlt = histl(entry(t));
-        const float* __restrict__ hpt = histp(entry(t));
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           MT lcur[K], rr[K];
-          float pcur[K], qrc[K];
-          load_vec<K>(hlt + g * K + opaque(lh), lcur);
-          load_vec<K>(hpt + g * K + opaque(lh), pcur);
+          float pcur[K], qr[K], qrc[K];
+          load_vec<K>(histl(e) + g * (LPS * K) + opaque(lh), lcur);
+          load_vec<K>(histp(e) + g * (LPS * K) + opaque(lh), pcur);
           load_vec<K>(msgl + K * (p + g * LPS), rr);
-          load_vec<K>(msgp + K * (p + g * LPS), qrc);
+          load_vec<K>(msgp + K * (p + g * LPS), qr);
 #pragma unroll
           for (int r = 0; r < K; ++r) {
             rr[r] -= shp;
-            qrc[r] -= gwh;  // Psi_t - g_t w_hat_t at the row offsets
+            qrc[r] = qr[r] - gwh;  // Psi_t - g_t w_hat_t at the row offsets
           }
+          store_vec<K>(histr(e) + g * (LPS * K) + opaque(lh), rr);
+          store_vec<K>(histq(e) + g * (LPS * K) + opaque(lh), qr);
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            float V[K], ac[K];
+            float V[K];
             vcol(g, a, V);
-            float* __restrict__ ua = accs + col(g, a);
-            load_vec<K>(ua + opaque(lo4), ac);
             MT y[K];
-            float dd[K];
             MT m = (MT)-INFINITY;
 #pragma unroll
             for (int r = 0; r < K; ++r) {
-              dd[r] = u - V[r];
               y[r] = emit<P>(u, V[r], rr[r], k.kap);
               m = tmax(m, y[r]);
             }
-            float e[K], t2[K];
+            float e4[K], t2[K];
 #pragma unroll
             for (int r = 0; r < K; ++r) {
-              e[r] = ex2((float)(y[r] - m));
+              e4[r] = ex2((float)(y[r] - m));
               t2[r] = __builtin_fmaf(gtp, V[r], qrc[r]);
             }
-            float cs = e[0], ps = e[0] * t2[0];
+            float cs = e4[0], ps = e4[0] * t2[0];
 #pragma unroll
             for (int r = 1; r < K; ++r) {
-              cs += e[r];
-              ps = __builtin_fmaf(e[r], t2[r], ps);
+              cs += e4[r];
+              ps = __builtin_fmaf(e4[r], t2[r], ps);
             }
             ro[g][a] = m + (MT)lg2(cs);
             qo[g][a] = ps * rcp_nr(cs);
@@ -1650,14 +1676,11 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             const float f = ex2((float)((m + lcur[a]) - LZ));
             const float pa = pcur[a] + hx;
             xs = __builtin_fmaf(f, __builtin_fmaf(pa, cs, ps), xs);
+            // sum_r c(s) E_t(s) over the column: f * sum_r V e (t2 + pa)
+            float cv = 0.f;
 #pragma unroll
-            for (int r = 0; r < K; ++r) {
-              const float gm = e[r] * f;
-              const float eh = gm * (t2[r] + pa);
-              gw = __builtin_fmaf(V[r], eh, gw);
-              ac[r] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, ac[r]));
-            }
-            store_vec<K>(ua + opaque(lo4), ac);
+            for (int r = 0; r < K; ++r) cv = __builtin_fmaf(V[r] * e4[r], t2[r] + pa, cv);
+            gw = __builtin_fmaf(f, cv, gw);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -1676,6 +1699,57 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         __syncthreads();
         shp = floor(v2[1]);
         Np += (double)shp;
+      }
+
+      // ---- phase C: codebook-gradient sums over the segment, block by block ------------------
+      // dF/dc(s) = sum_t [ g_t gamma_t(s) + (2/T)(w_t - c(s)) E_t(s) ], gamma_t(s) =
+      // 2^(emission + lam column + rho row - LZ_t), E_t(s) = gamma (X - xbar_t + h).
+      __syncthreads();  // lane 0's per-step LZ and xbar visible to every lane
+#pragma unroll 1
+      for (int g = 0; g < G; ++g) {
+        float Vg[K][K], ac[K][K];  // [r][a] codebook values, [a][r] sums
+        vblock(g, Vg);
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          const float* __restrict__ ub = accs + col(g, a);
+          load_vec<K>(ub + opaque(lo4), ac[a]);
+        }
+#pragma unroll 2
+        for (long long t = t1 - 1; t >= t0; --t) {
+          const long long e = entry(t);
+          MT lc[K], rr[K];
+          float pc[K], qr[K];
+          load_vec<K>(histl(e) + g * (LPS * K) + opaque(lh), lc);
+          load_vec<K>(histp(e) + g * (LPS * K) + opaque(lh), pc);
+          load_vec<K>(histr(e) + g * (LPS * K) + opaque(lh), rr);
+          load_vec<K>(histq(e) + g * (LPS * K) + opaque(lh), qr);
+          const float u = k.sc * wb[t];
+          const float gt = gb[t];
+          const float gtp = gt * k.csc;
+          const float gwh = gt * whb[t];
+          const MT LZ = (MT)lzt[t];
+          const float hx = h - xbt[t];
+#pragma unroll
+          for (int r = 0; r < K; ++r) qr[r] -= gwh;
+#pragma unroll
+          for (int a = 0; a < K; ++a) {
+            const MT lz = lc[a] - LZ;
+            const float pa = pc[a] + hx;
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+              const float v = Vg[r][a];
+              const float dd = u - v;
+              const float gm = ex2((float)(emit<P>(u, v, rr[r], k.kap) + lz));
+              const float eh = gm * (__builtin_fmaf(gtp, v, qr[r]) + pa);
+              ac[a][r] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd, eh, ac[a][r]));
+            }
+          }
+        }
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          float* __restrict__ ub = accs + col(g, a);
+          store_vec<K>(ub + opaque(lo4), ac[a]);
+        }
       }
     }
   }
