@@ -108,8 +108,6 @@ struct Cfg {
   static constexpr int SPB = LPS < 64 ? 64 / LPS : 1;
   static constexpr int BLOCK = LPS < 64 ? 64 : LPS;
   static constexpr int NWAVES = BLOCK / 64;
-  // stream the codebook from L2 when a 16-wave block leaves too few registers for it
-  static constexpr bool SV = LPS >= 1024 && G * K * K > 16;
   // LDS per buffer: the MT message (+ the fp32 expectation message in the backward).
   static constexpr long long BUF_BYTES = (long long)SPB * M * ((long long)sizeof(MT) + (BWD ? 4 : 0));
   // Double-buffer the message arrays when both buffers fit in 128 KiB, else one buffer and a
@@ -245,13 +243,10 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ src, T* dst) {
   }
 }
 
-// Per-lane codebook values v(s) = sc * c(s) of the lane's K x K blocks. Register-resident when
-// they fit; for chains of 1024 lanes (16-wave blocks, so at most 128 VGPRs per lane) they are
-// re-read from the L2-resident codebook one block at a time instead.
-template <class C, bool STREAM = C::SV>
-struct CodebookLane;
+// Per-lane codebook values v(s) = sc * c(s) of the lane's K x K blocks, register-resident (the
+// 1024-lane kernels, which have no room for them, read them block by block instead).
 template <class C>
-struct CodebookLane<C, false> {
+struct CodebookLane {
   float v[C::G][C::K][C::K];
   __device__ __forceinline__ void init(const float* __restrict__ cb, float sc, int p) {
 #pragma unroll
@@ -266,27 +261,6 @@ struct CodebookLane<C, false> {
     for (int r = 0; r < C::K; ++r)
 #pragma unroll
       for (int a = 0; a < C::K; ++a) out[r][a] = v[g][r][a];
-  }
-};
-template <class C>
-struct CodebookLane<C, true> {
-  const float* __restrict__ cb;
-  float sc;
-  int p;
-  __device__ __forceinline__ void init(const float* __restrict__ c, float s, int lane) {
-    cb = c;
-    sc = s;
-    p = lane;
-  }
-  __device__ __forceinline__ void get(int g, float (&out)[C::K][C::K]) const {
-    const float* base = cb + C::K * (p + g * C::LPS);
-#pragma unroll
-    for (int a = 0; a < C::K; ++a) {
-      float tmp[C::K];
-      load_vec<C::K>(base + a * C::M, tmp);
-#pragma unroll
-      for (int r = 0; r < C::K; ++r) out[r][a] = sc * tmp[r];
-    }
   }
 };
 
@@ -627,6 +601,21 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
   }
 }
 
+// A lane offset made opaque to the optimiser at each use, so that addresses built from it are
+// formed where they are used instead of being hoisted out of the step loops as 64-bit address
+// registers (one pair per block column, which would not fit next to the messages).
+__device__ __forceinline__ unsigned opaque(unsigned x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// Pins a value's computation at this point. The step outputs are stored only after the chain
+// reduction's barrier; without the pin the compiler sinks their arithmetic past it and keeps
+// every intermediate of the step alive across the reduction.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // ---------------------------------------------------------------------------------------------
 // Forward for chains of 1024 lanes (one 16-wave block per chain, so at most 128 registers per
 // lane). There the lane's blocks do not fit in registers together with their messages, codebook
@@ -649,8 +638,18 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   __shared__ __attribute__((aligned(16))) MT msg[2][M];
   __shared__ double red[2 * C::NWAVES * 4];
   const int p = threadIdx.x;
-  CodebookLane<C, true> vsrc;
-  vsrc.init(cb, k.sc, p);
+  // codebook value of state K*(p + g*LPS) + r + a*M: block-uniform base + 32-bit lane offset
+  const unsigned lo4 = K * p;
+  auto vblock = [&](int g, float (&v)[K][K]) {  // v[r][a] of block g
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      float tmp[K];
+      const float* __restrict__ ub = cb + (g * K * LPS + a * M);
+      load_vec<K>(ub + opaque(lo4), tmp);
+#pragma unroll
+      for (int r = 0; r < K; ++r) v[r][a] = k.sc * tmp[r];
+    }
+  };
 
   const long long seg = CK ? seg_arg : 0;
   const long long ncp = seg ? (L + seg - 1) / seg : L;
@@ -660,7 +659,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * LPS * KG * 8);
   // history entries are block-major, [H][G][LPS][K]: block g of this lane in entry e is at
   // hist(e) + g*LPS*K
-  auto hist = [&](long long e) { return hs + (size_t)e * LPS * KG + K * p; };
+  auto hist = [&](long long e) { return hs + (size_t)e * LPS * KG + opaque(lo4); };
   int rp = 0;
 
   // units == B (one chain per unit), so every unit is a chain
@@ -693,7 +692,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       MT* __restrict__ dst = msg[cur ^ 1];
       MT mx = (MT)-INFINITY;
       float Vn[K][K];
-      vsrc.get(0, Vn);
+      vblock(0, Vn);
 #pragma unroll 1
       for (int g = 0; g < G; ++g) {
         float Vg[K][K];
@@ -701,7 +700,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         for (int r = 0; r < K; ++r)
 #pragma unroll
           for (int a = 0; a < K; ++a) Vg[r][a] = Vn[r][a];
-        if (g + 1 < G) vsrc.get(g + 1, Vn);
+        if (g + 1 < G) vblock(g + 1, Vn);
         MT lc[K];
 #pragma unroll
         for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
@@ -801,7 +800,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       }
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
       float Vn[K][K];
-      vsrc.get(0, Vn);
+      vblock(0, Vn);
       MT ln[K];
       load_vec<K>(hist(entry(t1 - 1)), ln);
       for (long long t = t1 - 1; t >= t0; --t) {
@@ -823,7 +822,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
 #pragma unroll
           for (int a = 0; a < K; ++a) lcur[a] = ln[a];
           // next block's codebook values and history entry (block 0 of step t - 1 after the last)
-          vsrc.get(g + 1 < G ? g + 1 : 0, Vn);
+          vblock(g + 1 < G ? g + 1 : 0, Vn);
           if (g + 1 < G)
             load_vec<K>(hist(entry(t)) + (g + 1) * (LPS * K), ln);
           else if (t > t0)
@@ -1313,21 +1312,6 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 // lane's backward rows are parked meanwhile in the history entry of the checkpoint after the
 // segment's, which the backward sweep no longer needs.
 // ---------------------------------------------------------------------------------------------
-// A lane offset made opaque to the optimiser at each use, so that addresses built from it are
-// formed where they are used instead of being hoisted out of the step loops as 64-bit address
-// registers (one pair per block column, which would not fit next to the messages).
-__device__ __forceinline__ unsigned opaque(unsigned x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-// Pins a value's computation at this point. The step outputs are stored only after the chain
-// reduction's barrier; without the pin the compiler sinks their arithmetic past it and keeps
-// every intermediate of the step alive across the reduction.
-template <class T>
-__device__ __forceinline__ void pin(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
 template <class C, bool CK>
 __global__ void __launch_bounds__(C::BLOCK)
 k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, long long B,

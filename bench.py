@@ -53,6 +53,14 @@ KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_d
                   "bcjr_soft_decoding_amd/csrc/internal.h", "bcjr_soft_decoding_amd/build.py"]
 
 
+def bwd_kernel_name(n: int, k: int) -> str:
+    """Name of the backward kernel that runs for (n, k) with fp32 messages: chains of 1024 lanes
+    (S / K^2 blocks of 32 states per lane needing more than 1024 lanes) use the wide kernel."""
+    ng = (1 << n) >> (2 * k)
+    g = max(min(max(32 >> (2 * k), 1), ng), ng // 1024)
+    return "k_sparse_bwd_wide" if ng // g >= 1024 else "k_sparse_bwd"
+
+
 def op_slots(kernel: str) -> float:
     o = OPS[kernel]
     return o["valu"] + TRANS_SLOTS * o["trans"]
@@ -95,7 +103,8 @@ def parse():
     ap.add_argument("--history", choices=["full", "ckpt"], default="full",
                     help="bitshift message histories: every step, or checkpoints + segment replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1536, help="chains timed on the CPU oracle")
+    ap.add_argument("--cpu-sample", type=int, default=1536,
+                    help="chains timed on the CPU oracle (at most CPU_SAMPLE_STATE_STEPS state-steps)")
     ap.add_argument("--cpu-sample-dense", type=int, default=64,
                     help="chains of the dense workload timed on the CPU oracle")
     ap.add_argument("--viterbi", action="store_true",
@@ -130,6 +139,15 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+# The oracle's sample is capped at this many state-steps (about 15 s of fp64 work on 16 host
+# threads), so that large trellises (S = 65536) do not hold the run for minutes.
+CPU_SAMPLE_STATE_STEPS = 1536 * 256 * 4096
+
+
+def cpu_sample_chains(args, wl):
+    return max(1, min(args.cpu_sample, wl.B, CPU_SAMPLE_STATE_STEPS // (wl.L * wl.S)))
 
 
 def cpu_baseline(wl, c, w, g, T, sample):
@@ -502,7 +520,7 @@ def bench_viterbi(args, wl):
     if not args.no_cpu_baseline:
         import oracle
         cores = oracle.set_threads(0)
-        sample = min(args.cpu_sample, B)
+        sample = cpu_sample_chains(args, wl)
         t1 = time.perf_counter()
         ref = oracle.viterbi(n, k, c_np, w_np[:sample])
         dt = time.perf_counter() - t1
@@ -610,7 +628,7 @@ def main():
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
         "roofline": {
             "bound": "alu",
-            "kernel": "k_sparse_bwd",
+            "kernel": bwd_kernel_name(n, k),
             "achieved": achieved,
             "peak": PEAK_TOPS,
             "unit": "Tops/s",
@@ -620,7 +638,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, c_np, w_np, g_np, T, min(args.cpu_sample, B))
+        out["cpu_baseline"] = cpu_baseline(wl, c_np, w_np, g_np, T, cpu_sample_chains(args, wl))
     print(json.dumps(out))
 
 
