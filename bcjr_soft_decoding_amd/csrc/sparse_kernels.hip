@@ -189,8 +189,9 @@ __device__ __forceinline__ void chain_reduce(T (&v)[NV], double* red, int& rp) {
   } else {
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = lanes_reduce<64>(v[i], (MASK >> i) & 1u);
-    // per-wave partials in their own type (the double buffer holds either)
-    T* r = reinterpret_cast<T*>(red) + rp * (C::NWAVES * 4);
+    // per-wave partials in their own type; the two halves of the double buffer are counted in
+    // doubles, so that a float reduction never lands in the half a double reduction just used
+    T* r = reinterpret_cast<T*>(red + rp * (C::NWAVES * 4));
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
