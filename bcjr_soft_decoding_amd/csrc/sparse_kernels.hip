@@ -244,6 +244,35 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ src, T* dst) {
   }
 }
 
+// The same copies with the non-temporal hint, for the 1024-lane backward's history streams
+// (written once, read once or twice a whole chain later): they then do not push the codebook,
+// which every block rereads each step, out of L2 (measured 4% faster at S = 65536).
+template <int N, class T>
+__device__ __forceinline__ void store_vec_nt(T* __restrict__ dst, const T* src) {
+  constexpr int V = 16 / (int)sizeof(T);
+  static_assert(N % V == 0, "whole 16-byte vectors");
+  using Vec = __attribute__((ext_vector_type(V))) T;
+#pragma unroll
+  for (int i = 0; i < N; i += V) {
+    Vec x;
+#pragma unroll
+    for (int j = 0; j < V; ++j) x[j] = src[i + j];
+    __builtin_nontemporal_store(x, reinterpret_cast<Vec*>(dst + i));
+  }
+}
+template <int N, class T>
+__device__ __forceinline__ void load_vec_nt(const T* __restrict__ src, T* dst) {
+  constexpr int V = 16 / (int)sizeof(T);
+  static_assert(N % V == 0, "whole 16-byte vectors");
+  using Vec = __attribute__((ext_vector_type(V))) T;
+#pragma unroll
+  for (int i = 0; i < N; i += V) {
+    const Vec x = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(src + i));
+#pragma unroll
+    for (int j = 0; j < V; ++j) dst[i + j] = x[j];
+  }
+}
+
 // Per-lane codebook values v(s) = sc * c(s) of the lane's K x K blocks, register-resident (the
 // 1024-lane kernels, which have no room for them, read them block by block instead).
 template <class C>
@@ -1352,6 +1381,15 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       for (int r = 0; r < K; ++r) v[r][a] = c4[r];
     }
   };
+  // the block's raw codebook values c[a][r] (scaled where used, so that a load issued a block
+  // ahead is not waited for at once)
+  auto cblock = [&](int g, float (&c)[K][K]) {
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      const float* __restrict__ ub = cb + col(g, a);
+      load_vec<K>(ub + opaque(lo4), c[a]);
+    }
+  };
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -1415,10 +1453,16 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           lc[a] = msgl[p + g * LPS + a * NG] - sh;
           pc[a] = msgp[p + g * LPS + a * NG];
         }
-        store_vec<K>(histl(e) + g * (LPS * K) + opaque(lh), lc);
-        store_vec<K>(histp(e) + g * (LPS * K) + opaque(lh), pc);
+        store_vec_nt<K>(histl(e) + g * (LPS * K) + opaque(lh), lc);
+        store_vec_nt<K>(histp(e) + g * (LPS * K) + opaque(lh), pc);
       }
     };
+    // Loads and stores share one in-order completion counter (vmcnt), so waiting for a load
+    // also waits for every store issued before it. The steps below therefore issue each block's
+    // loads one block ahead, before the stores of the block being computed. Vn holds the next
+    // block's codebook values (block 0 when a run of steps starts: the codebook is fixed, so the
+    // last block of a step loads block 0 for the next).
+    float Vn[K][K];  // raw, [a][r]
     // One forward step (lam, Phi) of step t -> raw rows of step t + 1, written over the buffer
     // once every lane has read; records the inputs as entry e (e >= 0); returns the outputs'
     // chain-wide maximum.
@@ -1426,20 +1470,28 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       const float u = k.sc * wb[t];
       const float gtp = gb[t] * k.csc;   // g_t c(s) = gtp * v(s)
       const float gwh = gb[t] * whb[t];  // g_t w_hat_t
-      if (e >= 0) record(e);  // (before the arithmetic, which then has no branch in it)
       MT lo[G][K];
       float po[G][K];
       MT mx = (MT)-INFINITY;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float Vg[K][K];
-        vblock(g, Vg);
+#pragma unroll
+        for (int r = 0; r < K; ++r)
+#pragma unroll
+          for (int a = 0; a < K; ++a) Vg[r][a] = k.sc * Vn[a][r];
+        cblock((g + 1) % G, Vn);
         MT lc[K];
-        float pcc[K];
+        float pc[K], pcc[K];
 #pragma unroll
         for (int a = 0; a < K; ++a) {
           lc[a] = msgl[p + g * LPS + a * NG] - sh;
-          pcc[a] = msgp[p + g * LPS + a * NG] - gwh;
+          pc[a] = msgp[p + g * LPS + a * NG];
+          pcc[a] = pc[a] - gwh;
+        }
+        if (e >= 0) {
+          store_vec_nt<K>(histl(e) + g * (LPS * K) + opaque(lh), lc);
+          store_vec_nt<K>(histp(e) + g * (LPS * K) + opaque(lh), pc);
         }
 #pragma unroll
         for (int r = 0; r < K; ++r) {
@@ -1480,6 +1532,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
     // ---- phase A: lam and Phi, t = 0 .. L-1, plus one step to t = L -------------------------
     double N = 0.0;
     MT shL = (MT)0;
+    cblock(0, Vn);
     for (long long t = 0; t < L; ++t) {
       if (p == 0) ns[t] = N;
       const long long e = seg == 0 ? t : (t % seg == 0 ? t / seg : -1);
@@ -1556,8 +1609,8 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             float p4[K];
             load_vec<K>(msgl + K * (p + g * LPS), l4);
             load_vec<K>(msgp + K * (p + g * LPS), p4);
-            store_vec<K>(histl(sgi + 1) + g * (LPS * K) + opaque(lh), l4);
-            store_vec<K>(histp(sgi + 1) + g * (LPS * K) + opaque(lh), p4);
+            store_vec_nt<K>(histl(sgi + 1) + g * (LPS * K) + opaque(lh), l4);
+            store_vec_nt<K>(histp(sgi + 1) + g * (LPS * K) + opaque(lh), p4);
           }
         }
         __syncthreads();
@@ -1566,8 +1619,8 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           float q0[KG];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            load_vec<K>(histl(sgi) + g * (LPS * K) + opaque(lh), c0 + g * K);
-            load_vec<K>(histp(sgi) + g * (LPS * K) + opaque(lh), q0 + g * K);
+            load_vec_nt<K>(histl(sgi) + g * (LPS * K) + opaque(lh), c0 + g * K);
+            load_vec_nt<K>(histp(sgi) + g * (LPS * K) + opaque(lh), q0 + g * K);
           }
 #pragma unroll
           for (int g = 0; g < G; ++g)
@@ -1579,6 +1632,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         }
         __syncthreads();
         sh = (MT)0;
+        cblock(0, Vn);
         for (long long t = t0; t + 1 < t1; ++t) sh = floor(advance(t, ncp + (t - t0)));
         record(ncp + (t1 - 1 - t0));
         __syncthreads();
@@ -1587,8 +1641,8 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           float q1[KG];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            load_vec<K>(histl(sgi + 1) + g * (LPS * K) + opaque(lh), c1 + g * K);
-            load_vec<K>(histp(sgi + 1) + g * (LPS * K) + opaque(lh), q1 + g * K);
+            load_vec_nt<K>(histl(sgi + 1) + g * (LPS * K) + opaque(lh), c1 + g * K);
+            load_vec_nt<K>(histp(sgi + 1) + g * (LPS * K) + opaque(lh), q1 + g * K);
           }
           set_rows(c1, q1);
         } else {
@@ -1596,6 +1650,13 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         }
       }
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
+      // block-ahead loads (see advance): the next block's codebook values and history entry
+      float Vb[K][K];  // raw, [a][r]
+      MT hln[K];
+      float hpn[K];
+      cblock(0, Vb);
+      load_vec_nt<K>(histl(entry(t1 - 1)) + opaque(lh), hln);
+      load_vec_nt<K>(histp(entry(t1 - 1)) + opaque(lh), hpn);
       for (long long t = t1 - 1; t >= t0; --t) {
         const double Nt = ns[t];
         const float u = k.sc * wb[t];
@@ -1618,9 +1679,22 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           MT lcur[K], rr[K];
-          float pcur[K], qr[K], qrc[K];
-          load_vec<K>(histl(e) + g * (LPS * K) + opaque(lh), lcur);
-          load_vec<K>(histp(e) + g * (LPS * K) + opaque(lh), pcur);
+          float pcur[K], qr[K], qrc[K], Vg[K][K];
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            lcur[i] = hln[i];
+            pcur[i] = hpn[i];
+#pragma unroll
+            for (int a = 0; a < K; ++a) Vg[i][a] = k.sc * Vb[a][i];
+          }
+          {  // the next block's loads, before this block's stores (the block after the
+             // segment's last one re-reads an entry of this segment, which is harmless)
+            const long long en = g + 1 < G ? e : entry(t > t0 ? t - 1 : t);
+            const int gn = (g + 1) % G;
+            cblock(gn, Vb);
+            load_vec_nt<K>(histl(en) + gn * (LPS * K) + opaque(lh), hln);
+            load_vec_nt<K>(histp(en) + gn * (LPS * K) + opaque(lh), hpn);
+          }
           load_vec<K>(msgl + K * (p + g * LPS), rr);
           load_vec<K>(msgp + K * (p + g * LPS), qr);
 #pragma unroll
@@ -1628,12 +1702,13 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             rr[r] -= shp;
             qrc[r] = qr[r] - gwh;  // Psi_t - g_t w_hat_t at the row offsets
           }
-          store_vec<K>(histr(e) + g * (LPS * K) + opaque(lh), rr);
-          store_vec<K>(histq(e) + g * (LPS * K) + opaque(lh), qr);
+          store_vec_nt<K>(histr(e) + g * (LPS * K) + opaque(lh), rr);
+          store_vec_nt<K>(histq(e) + g * (LPS * K) + opaque(lh), qr);
 #pragma unroll
           for (int a = 0; a < K; ++a) {
             float V[K];
-            vcol(g, a, V);
+#pragma unroll
+            for (int r = 0; r < K; ++r) V[r] = Vg[r][a];
             MT y[K];
             MT m = (MT)-INFINITY;
 #pragma unroll
@@ -1699,15 +1774,27 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           const float* __restrict__ ub = accs + col(g, a);
           load_vec<K>(ub + opaque(lo4), ac[a]);
         }
-#pragma unroll 2
+        // the block's four recorded rows, one step ahead of the arithmetic
+        MT lcn[K], rrn[K];
+        float pcn[K], qrn[K];
+        auto rows_at = [&](long long e) {
+          load_vec_nt<K>(histl(e) + g * (LPS * K) + opaque(lh), lcn);
+          load_vec_nt<K>(histp(e) + g * (LPS * K) + opaque(lh), pcn);
+          load_vec_nt<K>(histr(e) + g * (LPS * K) + opaque(lh), rrn);
+          load_vec_nt<K>(histq(e) + g * (LPS * K) + opaque(lh), qrn);
+        };
+        rows_at(entry(t1 - 1));
         for (long long t = t1 - 1; t >= t0; --t) {
-          const long long e = entry(t);
           MT lc[K], rr[K];
           float pc[K], qr[K];
-          load_vec<K>(histl(e) + g * (LPS * K) + opaque(lh), lc);
-          load_vec<K>(histp(e) + g * (LPS * K) + opaque(lh), pc);
-          load_vec<K>(histr(e) + g * (LPS * K) + opaque(lh), rr);
-          load_vec<K>(histq(e) + g * (LPS * K) + opaque(lh), qr);
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            lc[i] = lcn[i];
+            rr[i] = rrn[i];
+            pc[i] = pcn[i];
+            qr[i] = qrn[i];
+          }
+          rows_at(entry(t > t0 ? t - 1 : t));
           const float u = k.sc * wb[t];
           const float gt = gb[t];
           const float gtp = gt * k.csc;
