@@ -397,9 +397,14 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int a = 0; a < K; ++a) lc[g][a] = (p + g * LPS + a * NG == i0) ? (MT)0 : (MT)-kFar;
     }
 
+    // The step's weight is loaded a step ahead, before the previous step's history stores:
+    // loads and stores share one in-order completion counter, so a load issued after them
+    // would also wait for the stores. wnx holds w_t when advance(t) starts.
+    float wnx = wb[0];
     // One forward step: the column offsets lc of step t -> those of step t + 1 (t < L - 1).
     auto advance = [&](long long t) {
-      const float u = k.sc * wb[t];
+      const float u = k.sc * wnx;
+      wnx = wb[t + 1 < L ? t + 1 : t];
       MT out[G][K];
       MT mx = (MT)-INFINITY;
 #pragma unroll
@@ -443,7 +448,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         if (p == 0) ns[t * SPB + q] = N;
       }
       if (t == L - 1) {
-        const float u = k.sc * wb[t];
+        const float u = k.sc * wnx;
         MT out[G][K];
         MT mx = (MT)-INFINITY;
 #pragma unroll
@@ -539,6 +544,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       const long long t1 = seg ? (t0 + seg < L ? t0 + seg : L) : L;
       if (CK) {
         load_vec<KG>(hist(sgi), &lc[0][0]);
+        wnx = wb[t0];
         for (long long t = t0; t < t1; ++t) {
           store_vec<KG>(hist(ncp + (t - t0)), &lc[0][0]);
           if (t + 1 < t1) advance(t);
@@ -1020,11 +1026,21 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         }
     }
 
+    // The step's inputs are loaded a step ahead, before the previous step's history stores
+    // (loads and stores share one in-order completion counter): wn, gn, hn hold w_t, g_t and
+    // w_hat_t when advance(t) starts.
+    float wn = wb[0], gn = gb[0], hn = whb[0];
+    auto inputs_at = [&](long long t) {
+      wn = wb[t];
+      gn = gb[t];
+      hn = whb[t];
+    };
     // One forward step: (lam, Phi) column offsets of step t -> those of step t + 1 (t < L - 1).
     auto advance = [&](long long t) {
-      const float u = k.sc * wb[t];
-      const float gtp = gb[t] * k.csc;     // g_t c(s) = gtp * v(s)
-      const float gwh = gb[t] * whb[t];    // g_t w_hat_t
+      const float u = k.sc * wn;
+      const float gtp = gn * k.csc;     // g_t c(s) = gtp * v(s)
+      const float gwh = gn * hn;        // g_t w_hat_t
+      inputs_at(t + 1 < L ? t + 1 : t);
       MT out[G][K];
       float pout[G][K];
       float pcc[G][K];  // Phi_t - g_t w_hat_t at the column offsets
@@ -1185,6 +1201,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       if (CK) {
         load_vec<KG>(histl(sgi), &lc[0][0]);
         load_vec<KG>(histp(sgi), &pc[0][0]);
+        inputs_at(t0);
         for (long long t = t0; t < t1; ++t) {
           store_vec<KG>(histl(ncp + (t - t0)), &lc[0][0]);
           store_vec<KG>(histp(ncp + (t - t0)), &pc[0][0]);
