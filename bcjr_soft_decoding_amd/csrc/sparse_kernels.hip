@@ -676,15 +676,21 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   const int p = threadIdx.x;
   // codebook value of state K*(p + g*LPS) + r + a*M: block-uniform base + 32-bit lane offset
   const unsigned lo4 = K * p;
-  auto vblock = [&](int g, float (&v)[K][K]) {  // v[r][a] of block g
+  // Raw codebook values c[a][r] of block g, loaded a block ahead and scaled where used: loads
+  // and stores share one in-order completion counter, so a load must be issued before the
+  // stores it should not wait for, and not be consumed right after it is issued.
+  auto cblock = [&](int g, float (&c)[K][K]) {
 #pragma unroll
     for (int a = 0; a < K; ++a) {
-      float tmp[K];
       const float* __restrict__ ub = cb + (g * K * LPS + a * M);
-      load_vec<K>(ub + opaque(lo4), tmp);
-#pragma unroll
-      for (int r = 0; r < K; ++r) v[r][a] = k.sc * tmp[r];
+      load_vec<K>(ub + opaque(lo4), c[a]);
     }
+  };
+  auto scaled = [&](const float (&c)[K][K], float (&v)[K][K]) {  // v[r][a] = sc * c[a][r]
+#pragma unroll
+    for (int r = 0; r < K; ++r)
+#pragma unroll
+      for (int a = 0; a < K; ++a) v[r][a] = k.sc * c[a][r];
   };
 
   const long long seg = CK ? seg_arg : 0;
@@ -720,23 +726,24 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         store_vec<K>(hist(e) + g * (LPS * K), lc);
       }
     };
+    // Loaded ahead of their use: the next block's raw codebook values (block 0 when a run of
+    // steps starts, and after a step's last block) and the next step's weight (wn = w_t when
+    // fstep(t) starts).
+    float Vn[K][K];
+    float wn = 0.f;
     // One forward step: offsets of step t -> raw outputs of step t + 1 in msg[cur ^ 1]; records
     // the offsets as history entry e (e >= 0) and returns the outputs' chain-wide maximum.
     auto fstep = [&](long long t, long long e) -> MT {
-      const float u = k.sc * wb[t];
+      const float u = k.sc * wn;
+      wn = wb[t + 1 < L ? t + 1 : t];
       const MT* __restrict__ src = msg[cur];
       MT* __restrict__ dst = msg[cur ^ 1];
       MT mx = (MT)-INFINITY;
-      float Vn[K][K];
-      vblock(0, Vn);
 #pragma unroll 1
       for (int g = 0; g < G; ++g) {
         float Vg[K][K];
-#pragma unroll
-        for (int r = 0; r < K; ++r)
-#pragma unroll
-          for (int a = 0; a < K; ++a) Vg[r][a] = Vn[r][a];
-        if (g + 1 < G) vblock(g + 1, Vn);
+        scaled(Vn, Vg);
+        cblock(g + 1 < G ? g + 1 : 0, Vn);
         MT lc[K];
 #pragma unroll
         for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
@@ -766,6 +773,8 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
 
     // ---- phase A: forward messages, t = 0 .. L-1 ---------------------------------------------
     double N = 0.0, lz2 = 0.0;
+    cblock(0, Vn);
+    wn = wb[0];
     for (long long t = 0;; ++t) {
       if (p == 0) ns[t] = N;
       const long long e = seg == 0 ? t : (t % seg == 0 ? t / seg : -1);
@@ -824,6 +833,8 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         __syncthreads();
         cur = 0;
         sh = (MT)0;
+        cblock(0, Vn);
+        wn = wb[t0];
         for (long long t = t0; t + 1 < t1; ++t) {
           const MT mx = fstep(t, ncp + (t - t0));
           sh = floor(mx);
@@ -835,8 +846,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         for (int g = 0; g < G; ++g) store_vec<K>(msg[rb] + K * (p + g * LPS), keep[g]);
       }
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
-      float Vn[K][K];
-      vblock(0, Vn);
+      cblock(0, Vn);
       MT ln[K];
       load_vec<K>(hist(entry(t1 - 1)), ln);
       for (long long t = t1 - 1; t >= t0; --t) {
@@ -851,18 +861,16 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         for (int g = 0; g < G; ++g) {
           float Vg[K][K];
           MT lcur[K];
-#pragma unroll
-          for (int r = 0; r < K; ++r)
-#pragma unroll
-            for (int a = 0; a < K; ++a) Vg[r][a] = Vn[r][a];
+          scaled(Vn, Vg);
 #pragma unroll
           for (int a = 0; a < K; ++a) lcur[a] = ln[a];
-          // next block's codebook values and history entry (block 0 of step t - 1 after the last)
-          vblock(g + 1 < G ? g + 1 : 0, Vn);
-          if (g + 1 < G)
-            load_vec<K>(hist(entry(t)) + (g + 1) * (LPS * K), ln);
-          else if (t > t0)
-            load_vec<K>(hist(entry(t - 1)), ln);
+          // next block's codebook values and history entry (block 0 of step t - 1 after the
+          // last; after the segment's last step this re-reads an entry of the segment)
+          cblock(g + 1 < G ? g + 1 : 0, Vn);
+          {
+            const long long en = g + 1 < G ? entry(t) : entry(t > t0 ? t - 1 : t);
+            load_vec<K>(hist(en) + ((g + 1) % G) * (LPS * K), ln);
+          }
           MT rr[K];
           load_vec<K>(src + K * (p + g * LPS), rr);
 #pragma unroll
