@@ -358,12 +358,17 @@ k_dense_sweep(SweepArgs A) {
       }
     };
 
-    auto step = [&](long long j, float (&ra)[2], float (&rb)[2]) {
+    auto step = [&](long long j, float (&rn)[2], float (&rbn)[2]) {
       const long long t = FWD ? j : L - 1 - j;
       const int buf = (int)(j & 1);
       const long long cidx = j / kChunk;
       const int tt = (int)(j - cidx * kChunk);
       const float* scb = sc[cidx & 1] + tt * NQ * 4 + ch;
+      // this step's history values, then the loads of step j + 2 into the same registers:
+      // issued before this step's stores, since loads and stores share one in-order
+      // completion counter and a later wait for the loads would also wait for those stores
+      const float ra[2] = {rn[0], rn[1]}, rb[2] = {rbn[0], rbn[1]};
+      hist_load(j + 2, rn, rbn);
       float o[2] = {0.f, 0.f};
       if (j > 0) {
         product<C>(xs[buf ^ 1], m, l, o);
@@ -452,7 +457,6 @@ k_dense_sweep(SweepArgs A) {
       if (tt == kChunk - 1 && cidx + 1 < nch) stage_store((int)((cidx + 1) & 1));
       __syncthreads();
       if (tt == 0 && cidx + 1 < nch) stage_load(cidx + 1);
-      hist_load(j + 2, ra, rb);
     };
 
     float ra0[2] = {0.f, 0.f}, rb0[2] = {0.f, 0.f}, ra1[2] = {0.f, 0.f}, rb1[2] = {0.f, 0.f};
