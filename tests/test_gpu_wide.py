@@ -39,6 +39,9 @@ CASES = [
     (15, 280, 20, 0.2, ("full",)),           # 2 blocks per lane
     (15, 280, 20, 0.005, ("full", "ckpt")),  # fp64 messages
     (14, 300, 16, 0.005, ("full",)),         # fp64 messages, 1 block per lane
+    (16, 3, 1, 0.3, ("full", "ckpt")),       # L = 1: no recursion step at all
+    (16, 3, 2, 0.3, ("full", "ckpt")),       # L = 2: one step each way
+    (15, 2, 1, 0.005, ("full", "ckpt")),     # L = 1 with fp64 messages
 ]
 
 
