@@ -275,6 +275,8 @@ def bench_dense(args, wl):
         "config": {"workload": wl.name, "B": B, "L": L, "S": S, "T": T, "trellis": "dense",
                    "parallelism": "single-gpu"},
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
+        # trellis edges per second: every state follows every state, S per state-step
+        "edges_per_s": value * S,
         "roofline": {
             "bound": "mfma",
             "kernel": "bcjr_dense_backward (k_dense_sweep Psi + Phi, k_dense_theta_gemm)",
@@ -451,6 +453,7 @@ def bench_scan(args, wl):
                    "segment_length": seg, "segments": -(-L // seg),
                    "workspace_bytes": int(wsf.numel() + wsb.numel()), "parallelism": "single-gpu"},
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
+        "edges_per_s": value * (1 << k),
         "sequential_fwd_bwd_ms": seq_ms,
         "speedup_vs_sequential": seq_ms / (elapsed * 1e3 / args.steps),
         "max_rel_diff_vs_sequential": {"w_hat": diff_w, "grad_w": diff_g},
@@ -626,6 +629,8 @@ def main():
                    "history": args.history, "workspace_bytes": int(wsf.numel() + wsb.numel()),
                    "parallelism": "single-gpu"},
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
+        # trellis edges per second: K per state-step
+        "edges_per_s": value * (1 << k),
         "roofline": {
             "bound": "alu",
             "kernel": bwd_kernel_name(n, k),
