@@ -276,7 +276,7 @@ def bench_dense(args, wl):
                    "parallelism": "single-gpu"},
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
         # trellis edges per second: every state follows every state, S per state-step
-        "edges_per_s": value * S,
+        "edges_per_s": B * L * S / (elapsed / args.steps) * S,
         "roofline": {
             "bound": "mfma",
             "kernel": "bcjr_dense_backward (k_dense_sweep Psi + Phi, k_dense_theta_gemm)",
@@ -453,7 +453,7 @@ def bench_scan(args, wl):
                    "segment_length": seg, "segments": -(-L // seg),
                    "workspace_bytes": int(wsf.numel() + wsb.numel()), "parallelism": "single-gpu"},
         "kernels_ms": {"forward": fwd_ms, "backward": bwd_ms},
-        "edges_per_s": value * (1 << k),
+        "edges_per_s": B * L * S / (elapsed / args.steps) * (1 << k),
         "sequential_fwd_bwd_ms": seq_ms,
         "speedup_vs_sequential": seq_ms / (elapsed * 1e3 / args.steps),
         "max_rel_diff_vs_sequential": {"w_hat": diff_w, "grad_w": diff_g},
