@@ -91,6 +91,51 @@ __device__ __forceinline__ typename P::MT emit(float u, float v, typename P::MT 
     return __builtin_fmaf(-d, d, off);
   }
 }
+// The scaled difference u - v = u - sc * c from a raw codebook value c, as one fma (with fp64
+// messages sc = 1, and this is u - c exactly), and the emission from it.
+template <class P>
+__device__ __forceinline__ float sdiff(float u, float sc, float c) {
+  if constexpr (P::kPrecise) {
+    (void)sc;
+    return u - c;
+  } else {
+    return __builtin_fmaf(-sc, c, u);
+  }
+}
+template <class P>
+__device__ __forceinline__ typename P::MT emit_d(float d, typename P::MT off, double kap) {
+  if constexpr (P::kPrecise) {
+    const double dd = (double)d;
+    return __builtin_fma(-(kap * dd), dd, off);
+  } else {
+    (void)kap;
+    return __builtin_fmaf(-d, d, off);
+  }
+}
+// Runs body(g, in) over a lane's G blocks while the inputs of the block after g are loaded by
+// load(g + 1, in') into the other of two register sets, used in turn, so that inputs loaded
+// ahead are never copied between registers; load(G, .) fetches block 0 of the next step.
+template <int G, class In, class Load, class Body>
+__device__ __forceinline__ void over_blocks(In& a, In& b, Load&& load, Body&& body) {
+  if constexpr (G == 1) {
+    b = a;
+    load(1, a);
+    body(0, b);
+  } else {
+    static_assert(G % 2 == 0, "blocks are visited in pairs");
+#pragma unroll 1
+    for (int g = 0; g < G; g += 2) {
+      // the barriers keep the scheduler from interleaving the two blocks (which would hold
+      // both blocks' intermediates at once)
+      load(g + 1, b);
+      body(g, a);
+      __builtin_amdgcn_sched_barrier(0);
+      load(g + 2, a);
+      body(g + 1, b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
 // max through the hardware max instructions (v_max3_f32 / v_max_f64)
 __device__ __forceinline__ float tmax(float a, float b) { return fmaxf(a, b); }
 __device__ __forceinline__ double tmax(double a, double b) { return fmax(a, b); }
@@ -644,6 +689,15 @@ __device__ __forceinline__ unsigned opaque(unsigned x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// A per-step scalar read through the vector memory path, behind a zero offset the compiler
+// cannot see through. A scalar load shares its completion counter with LDS accesses, and scalar
+// loads complete out of order, so the first LDS wait after a scalar load issued a step ahead
+// also waits for that load; a vector load is counted in order with the other vector memory
+// accesses and is waited for only where it is used.
+template <class T>
+__device__ __forceinline__ T vload(const T* __restrict__ base, long long i) {
+  return base[i + opaque(0u)];
+}
 // Pins a value's computation at this point. The step outputs are stored only after the chain
 // reduction's barrier; without the pin the compiler sinks their arithmetic past it and keeps
 // every intermediate of the step alive across the reduction.
@@ -676,9 +730,9 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   const int p = threadIdx.x;
   // codebook value of state K*(p + g*LPS) + r + a*M: block-uniform base + 32-bit lane offset
   const unsigned lo4 = K * p;
-  // Raw codebook values c[a][r] of block g, loaded a block ahead and scaled where used: loads
-  // and stores share one in-order completion counter, so a load must be issued before the
-  // stores it should not wait for, and not be consumed right after it is issued.
+  // Raw codebook values c[a][r] of block g, loaded a block ahead (over_blocks): loads and
+  // stores share one in-order completion counter, so a load must be issued before the stores
+  // it should not wait for, and not be consumed right after it is issued.
   auto cblock = [&](int g, float (&c)[K][K]) {
 #pragma unroll
     for (int a = 0; a < K; ++a) {
@@ -686,11 +740,12 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       load_vec<K>(ub + opaque(lo4), c[a]);
     }
   };
-  auto scaled = [&](const float (&c)[K][K], float (&v)[K][K]) {  // v[r][a] = sc * c[a][r]
-#pragma unroll
-    for (int r = 0; r < K; ++r)
-#pragma unroll
-      for (int a = 0; a < K; ++a) v[r][a] = k.sc * c[a][r];
+  struct FIn {  // inputs of a forward block loaded ahead
+    float c[K][K];
+  };
+  struct BIn {  // inputs of a backward block loaded ahead: codebook values and history entry
+    float c[K][K];
+    MT l[K];
   };
 
   const long long seg = CK ? seg_arg : 0;
@@ -727,45 +782,43 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       }
     };
     // Loaded ahead of their use: the next block's raw codebook values (block 0 when a run of
-    // steps starts, and after a step's last block) and the next step's weight (wn = w_t when
-    // fstep(t) starts).
-    float Vn[K][K];
+    // steps starts, and after a step's last block; fa, with fb the second register set) and
+    // the next step's weight (wn = w_t when fstep(t) starts).
+    FIn fa, fb;
     float wn = 0.f;
     // One forward step: offsets of step t -> raw outputs of step t + 1 in msg[cur ^ 1]; records
     // the offsets as history entry e (e >= 0) and returns the outputs' chain-wide maximum.
     auto fstep = [&](long long t, long long e) -> MT {
       const float u = k.sc * wn;
-      wn = wb[t + 1 < L ? t + 1 : t];
+      wn = vload(wb, t + 1 < L ? t + 1 : t);
       const MT* __restrict__ src = msg[cur];
       MT* __restrict__ dst = msg[cur ^ 1];
       MT mx = (MT)-INFINITY;
-#pragma unroll 1
-      for (int g = 0; g < G; ++g) {
-        float Vg[K][K];
-        scaled(Vn, Vg);
-        cblock(g + 1 < G ? g + 1 : 0, Vn);
-        MT lc[K];
+      over_blocks<G>(
+          fa, fb, [&](int gn, FIn& in) { cblock(gn < G ? gn : 0, in.c); },
+          [&](int g, const FIn& in) {
+            MT lc[K];
 #pragma unroll
-        for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
-        if (e >= 0) store_vec<K>(hist(e) + g * (LPS * K), lc);
-        MT out[K];
+            for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
+            if (e >= 0) store_vec<K>(hist(e) + g * (LPS * K), lc);
+            MT out[K];
 #pragma unroll
-        for (int r = 0; r < K; ++r) {
-          MT x[K];
-          MT m = (MT)-INFINITY;
+            for (int r = 0; r < K; ++r) {
+              MT x[K];
+              MT m = (MT)-INFINITY;
 #pragma unroll
-          for (int a = 0; a < K; ++a) {
-            x[a] = emit<P>(u, Vg[r][a], lc[a], k.kap);
-            m = tmax(m, x[a]);
-          }
-          float s = ex2((float)(x[0] - m));
+              for (int a = 0; a < K; ++a) {
+                x[a] = emit_d<P>(sdiff<P>(u, k.sc, in.c[a][r]), lc[a], k.kap);
+                m = tmax(m, x[a]);
+              }
+              float s = ex2((float)(x[0] - m));
 #pragma unroll
-          for (int a = 1; a < K; ++a) s += ex2((float)(x[a] - m));
-          out[r] = m + (MT)lg2(s);
-          mx = tmax(mx, out[r]);
-        }
-        store_vec<K>(dst + K * (p + g * LPS), out);
-      }
+              for (int a = 1; a < K; ++a) s += ex2((float)(x[a] - m));
+              out[r] = m + (MT)lg2(s);
+              mx = tmax(mx, out[r]);
+            }
+            store_vec<K>(dst + K * (p + g * LPS), out);
+          });
       MT v1[1] = {mx};
       chain_reduce<C, 1, 1u>(v1, red, rp);
       return v1[0];
@@ -773,8 +826,8 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
 
     // ---- phase A: forward messages, t = 0 .. L-1 ---------------------------------------------
     double N = 0.0, lz2 = 0.0;
-    cblock(0, Vn);
-    wn = wb[0];
+    cblock(0, fa.c);
+    wn = vload(wb, 0);
     for (long long t = 0;; ++t) {
       if (p == 0) ns[t] = N;
       const long long e = seg == 0 ? t : (t % seg == 0 ? t / seg : -1);
@@ -833,8 +886,8 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         __syncthreads();
         cur = 0;
         sh = (MT)0;
-        cblock(0, Vn);
-        wn = wb[t0];
+        cblock(0, fa.c);
+        wn = vload(wb, t0);
         for (long long t = t0; t + 1 < t1; ++t) {
           const MT mx = fstep(t, ncp + (t - t0));
           sh = floor(mx);
@@ -846,64 +899,71 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         for (int g = 0; g < G; ++g) store_vec<K>(msg[rb] + K * (p + g * LPS), keep[g]);
       }
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
-      cblock(0, Vn);
-      MT ln[K];
-      load_vec<K>(hist(entry(t1 - 1)), ln);
+      BIn ba, bb;  // block-ahead loads, two register sets in turn
+      cblock(0, ba.c);
+      load_vec<K>(hist(entry(t1 - 1)), ba.l);
+      // the step's scalars, loaded a step ahead (a load consumed at once would also wait for
+      // the stores issued before it)
+      double nsn = ns[t1 - 1];
+      float wn = vload(wb, t1 - 1);
       for (long long t = t1 - 1; t >= t0; --t) {
-        const double Nt = ns[t];
-        const float u = k.sc * wb[t];
+        const double Nt = nsn;
+        const float u = k.sc * wn;
+        {
+          const long long tp = t > t0 ? t - 1 : t;
+          nsn = ns[tp];
+          wn = vload(wb, tp);
+        }
         const MT LZ = (MT)((lz2 - Nt) - Np);
         const MT* __restrict__ src = msg[rb];
         MT* __restrict__ dst = msg[rb ^ 1];
         float num = 0.f, den = 0.f;
         MT mx = (MT)-INFINITY;
-#pragma unroll 1
-        for (int g = 0; g < G; ++g) {
-          float Vg[K][K];
-          MT lcur[K];
-          scaled(Vn, Vg);
+        over_blocks<G>(
+            ba, bb,
+            [&](int gn, BIn& in) {
+              // block 0 of step t - 1 after the last block (after the segment's last step this
+              // re-reads an entry of the segment)
+              cblock(gn < G ? gn : 0, in.c);
+              const long long en = gn < G ? entry(t) : entry(t > t0 ? t - 1 : t);
+              load_vec<K>(hist(en) + (gn < G ? gn : 0) * (LPS * K), in.l);
+            },
+            [&](int g, const BIn& in) {
+              MT rr[K];
+              load_vec<K>(src + K * (p + g * LPS), rr);
 #pragma unroll
-          for (int a = 0; a < K; ++a) lcur[a] = ln[a];
-          // next block's codebook values and history entry (block 0 of step t - 1 after the
-          // last; after the segment's last step this re-reads an entry of the segment)
-          cblock(g + 1 < G ? g + 1 : 0, Vn);
-          {
-            const long long en = g + 1 < G ? entry(t) : entry(t > t0 ? t - 1 : t);
-            load_vec<K>(hist(en) + ((g + 1) % G) * (LPS * K), ln);
-          }
-          MT rr[K];
-          load_vec<K>(src + K * (p + g * LPS), rr);
+              for (int r = 0; r < K; ++r) rr[r] -= shp;
 #pragma unroll
-          for (int r = 0; r < K; ++r) rr[r] -= shp;
+              for (int a = 0; a < K; ++a) {
+                MT y[K];
+                MT m = (MT)-INFINITY;
 #pragma unroll
-          for (int a = 0; a < K; ++a) {
-            MT y[K];
-            MT m = (MT)-INFINITY;
+                for (int r = 0; r < K; ++r) {
+                  y[r] = emit_d<P>(sdiff<P>(u, k.sc, in.c[a][r]), rr[r], k.kap);
+                  m = tmax(m, y[r]);
+                }
+                // cw: the column's weighted sum of raw codebook values
+                float e0 = ex2((float)(y[0] - m));
+                float cs = e0, cw = in.c[a][0] * e0;
 #pragma unroll
-            for (int r = 0; r < K; ++r) {
-              y[r] = emit<P>(u, Vg[r][a], rr[r], k.kap);
-              m = tmax(m, y[r]);
-            }
-            float e0 = ex2((float)(y[0] - m));
-            float cs = e0, cw = Vg[0][a] * e0;
-#pragma unroll
-            for (int r = 1; r < K; ++r) {
-              const float e = ex2((float)(y[r] - m));
-              cs += e;
-              cw = __builtin_fmaf(Vg[r][a], e, cw);
-            }
-            const MT ro = m + (MT)lg2(cs);
-            mx = tmax(mx, ro);
-            const float f = ex2((float)((m + lcur[a]) - LZ));
-            num = __builtin_fmaf(f, cw, num);
-            den = __builtin_fmaf(f, cs, den);
-            if (t > 0) dst[p + g * LPS + a * NG] = ro;
-          }
-        }
+                for (int r = 1; r < K; ++r) {
+                  const float e = ex2((float)(y[r] - m));
+                  cs += e;
+                  cw = __builtin_fmaf(in.c[a][r], e, cw);
+                }
+                const MT ro = m + (MT)lg2(cs);
+                mx = tmax(mx, ro);
+                const float f = ex2((float)((m + in.l[a]) - LZ));
+                num = __builtin_fmaf(f, cw, num);
+                den = __builtin_fmaf(f, cs, den);
+                // (at t = 0 the write is dead: the next chain starts behind a barrier)
+                dst[p + g * LPS + a * NG] = ro;
+              }
+            });
         MT v3[3] = {(MT)num, (MT)den, mx};
         chain_reduce<C, 3, 4u>(v3, red, rp);
         if (p == 0) {
-          const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
+          const float wh = (float)v3[0] / (float)v3[1];
           w_hat[b * L + t] = wh;
           saved_what[b * L + t] = wh;
         }
@@ -1390,22 +1450,6 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   const unsigned lo4 = K * p;
   float* __restrict__ accs = partial + (size_t)blockIdx.x * C::S;
   auto col = [](int g, int a) { return g * K * LPS + a * M; };
-  auto vcol = [&](int g, int a, float (&v)[K]) {  // codebook values of one block column
-    float tmp[K];
-    const float* __restrict__ ub = cb + col(g, a);
-    load_vec<K>(ub + opaque(lo4), tmp);
-#pragma unroll
-    for (int r = 0; r < K; ++r) v[r] = k.sc * tmp[r];
-  };
-  auto vblock = [&](int g, float (&v)[K][K]) {  // the whole block, v[r][a]
-#pragma unroll
-    for (int a = 0; a < K; ++a) {
-      float c4[K];
-      vcol(g, a, c4);
-#pragma unroll
-      for (int r = 0; r < K; ++r) v[r][a] = c4[r];
-    }
-  };
   // the block's raw codebook values c[a][r] (scaled where used, so that a load issued a block
   // ahead is not waited for at once)
   auto cblock = [&](int g, float (&c)[K][K]) {
@@ -1485,16 +1529,27 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
     // Loads and stores share one in-order completion counter (vmcnt), so waiting for a load
     // also waits for every store issued before it. The steps below therefore issue each block's
     // loads one block ahead, before the stores of the block being computed. Vn holds the next
-    // block's codebook values (block 0 when a run of steps starts: the codebook is fixed, so the
-    // last block of a step loads block 0 for the next).
+    // block's raw codebook values (block 0 when a run of steps starts: the codebook is fixed, so
+    // the last block of a step loads block 0 for the next). The block loops of advance and of
+    // phase B are unrolled (their outputs stay in registers across the chain reduction), so
+    // the values loaded ahead are renamed, not copied.
     float Vn[K][K];  // raw, [a][r]
+    // The step's scalars w_t, g_t, w_hat_t, likewise loaded a step ahead (steps_from(t) when
+    // a run of steps starts at t).
+    float wn = 0.f, gn = 0.f, whn = 0.f;
+    auto steps_from = [&](long long t) {
+      wn = vload(wb, t);
+      gn = vload(gb, t);
+      whn = vload(whb, t);
+    };
     // One forward step (lam, Phi) of step t -> raw rows of step t + 1, written over the buffer
     // once every lane has read; records the inputs as entry e (e >= 0); returns the outputs'
     // chain-wide maximum.
     auto advance = [&](long long t, long long e) -> MT {
-      const float u = k.sc * wb[t];
-      const float gtp = gb[t] * k.csc;   // g_t c(s) = gtp * v(s)
-      const float gwh = gb[t] * whb[t];  // g_t w_hat_t
+      const float u = k.sc * wn;
+      const float gt = gn;           // g_t c(s) from the raw codebook value
+      const float gwh = gn * whn;    // g_t w_hat_t
+      steps_from(t + 1 < L ? t + 1 : t);
       MT lo[G][K];
       float po[G][K];
       MT mx = (MT)-INFINITY;
@@ -1502,9 +1557,9 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       for (int g = 0; g < G; ++g) {
         float Vg[K][K];
 #pragma unroll
-        for (int r = 0; r < K; ++r)
+        for (int a = 0; a < K; ++a)
 #pragma unroll
-          for (int a = 0; a < K; ++a) Vg[r][a] = k.sc * Vn[a][r];
+          for (int r = 0; r < K; ++r) Vg[a][r] = Vn[a][r];
         cblock((g + 1) % G, Vn);
         MT lc[K];
         float pc[K], pcc[K];
@@ -1524,16 +1579,16 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           MT m = (MT)-INFINITY;
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            x[a] = emit<P>(u, Vg[r][a], lc[a], k.kap);
+            x[a] = emit_d<P>(sdiff<P>(u, k.sc, Vg[a][r]), lc[a], k.kap);
             m = tmax(m, x[a]);
           }
           float e0 = ex2((float)(x[0] - m));
-          float s = e0, ph = e0 * __builtin_fmaf(gtp, Vg[r][0], pcc[0]);
+          float s = e0, ph = e0 * __builtin_fmaf(gt, Vg[0][r], pcc[0]);
 #pragma unroll
           for (int a = 1; a < K; ++a) {
             const float ea = ex2((float)(x[a] - m));
             s += ea;
-            ph = __builtin_fmaf(ea, __builtin_fmaf(gtp, Vg[r][a], pcc[a]), ph);
+            ph = __builtin_fmaf(ea, __builtin_fmaf(gt, Vg[a][r], pcc[a]), ph);
           }
           lo[g][r] = m + (MT)lg2(s);
           po[g][r] = ph * rcp_nr(s);
@@ -1558,6 +1613,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
     double N = 0.0;
     MT shL = (MT)0;
     cblock(0, Vn);
+    steps_from(0);
     for (long long t = 0; t < L; ++t) {
       if (p == 0) ns[t] = N;
       const long long e = seg == 0 ? t : (t % seg == 0 ? t / seg : -1);
@@ -1658,6 +1714,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         __syncthreads();
         sh = (MT)0;
         cblock(0, Vn);
+        steps_from(t0);
         for (long long t = t0; t + 1 < t1; ++t) sh = floor(advance(t, ncp + (t - t0)));
         record(ncp + (t1 - 1 - t0));
         __syncthreads();
@@ -1682,12 +1739,19 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       cblock(0, Vb);
       load_vec_nt<K>(histl(entry(t1 - 1)) + opaque(lh), hln);
       load_vec_nt<K>(histp(entry(t1 - 1)) + opaque(lh), hpn);
+      double nsn = ns[t1 - 1];  // with steps_from: the step's scalars, a step ahead
+      steps_from(t1 - 1);
       for (long long t = t1 - 1; t >= t0; --t) {
-        const double Nt = ns[t];
-        const float u = k.sc * wb[t];
-        const float gt = gb[t];
-        const float gtp = gt * k.csc;
-        const float gwh = gt * whb[t];
+        const double Nt = nsn;
+        const float wt = wn;
+        const float u = k.sc * wn;
+        const float gt = gn;
+        const float gwh = gn * whn;
+        {
+          const long long tp = t > t0 ? t - 1 : t;
+          nsn = ns[tp];
+          steps_from(tp);
+        }
         const MT LZ = (MT)((lz2 - Nt) - Np);
         // E_t(s) = gamma (X - xbar + h) with X = Phi + g (c - w_hat) + Psi; xs sums it over the
         // states, so xs - h is the part of the mean of X that xbar did not remove
@@ -1704,13 +1768,13 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           MT lcur[K], rr[K];
-          float pcur[K], qr[K], qrc[K], Vg[K][K];
+          float pcur[K], qr[K], qrc[K], Vg[K][K];  // Vg raw, [a][r]
 #pragma unroll
           for (int i = 0; i < K; ++i) {
             lcur[i] = hln[i];
             pcur[i] = hpn[i];
 #pragma unroll
-            for (int a = 0; a < K; ++a) Vg[i][a] = k.sc * Vb[a][i];
+            for (int a = 0; a < K; ++a) Vg[a][i] = Vb[a][i];
           }
           {  // the next block's loads, before this block's stores (the block after the
              // segment's last one re-reads an entry of this segment, which is harmless)
@@ -1731,21 +1795,19 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           store_vec_nt<K>(histq(e) + g * (LPS * K) + opaque(lh), qr);
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            float V[K];
-#pragma unroll
-            for (int r = 0; r < K; ++r) V[r] = Vg[r][a];
+            const float (&V)[K] = Vg[a];
             MT y[K];
             MT m = (MT)-INFINITY;
 #pragma unroll
             for (int r = 0; r < K; ++r) {
-              y[r] = emit<P>(u, V[r], rr[r], k.kap);
+              y[r] = emit_d<P>(sdiff<P>(u, k.sc, V[r]), rr[r], k.kap);
               m = tmax(m, y[r]);
             }
             float e4[K], t2[K];
 #pragma unroll
             for (int r = 0; r < K; ++r) {
               e4[r] = ex2((float)(y[r] - m));
-              t2[r] = __builtin_fmaf(gtp, V[r], qrc[r]);
+              t2[r] = __builtin_fmaf(gt, V[r], qrc[r]);
             }
             float cs = e4[0], ps = e4[0] * t2[0];
 #pragma unroll
@@ -1761,7 +1823,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             const float f = ex2((float)((m + lcur[a]) - LZ));
             const float pa = pcur[a] + hx;
             xs = __builtin_fmaf(f, __builtin_fmaf(pa, cs, ps), xs);
-            // sum_r c(s) E_t(s) over the column: f * sum_r V e (t2 + pa)
+            // sum_r c(s) E_t(s) over the column: f * sum_r c e (t2 + pa)
             float cv = 0.f;
 #pragma unroll
             for (int r = 0; r < K; ++r) cv = __builtin_fmaf(V[r] * e4[r], t2[r] + pa, cv);
@@ -1772,7 +1834,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         MT v2[3] = {(MT)gw, mx, (MT)xs};
         chain_reduce<C, 3, 2u>(v2, red, rp);
         xbar += (float)v2[2] - h;
-        if (p == 0) grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+        if (p == 0) grad_w[b * L + t] = 2.0f * k.inv_t * ((float)v2[0] - h * wt);
         if (t == 0) break;
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -1792,55 +1854,62 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       __syncthreads();  // lane 0's per-step LZ and xbar visible to every lane
 #pragma unroll 1
       for (int g = 0; g < G; ++g) {
-        float Vg[K][K], ac[K][K];  // [r][a] codebook values, [a][r] sums
-        vblock(g, Vg);
+        float Vg[K][K], ac[K][K];  // raw codebook values and sums, both [a][r]
+        cblock(g, Vg);
 #pragma unroll
         for (int a = 0; a < K; ++a) {
           const float* __restrict__ ub = accs + col(g, a);
           load_vec<K>(ub + opaque(lo4), ac[a]);
         }
-        // the block's four recorded rows, one step ahead of the arithmetic
-        MT lcn[K], rrn[K];
-        float pcn[K], qrn[K];
-        auto rows_at = [&](long long e) {
-          load_vec_nt<K>(histl(e) + g * (LPS * K) + opaque(lh), lcn);
-          load_vec_nt<K>(histp(e) + g * (LPS * K) + opaque(lh), pcn);
-          load_vec_nt<K>(histr(e) + g * (LPS * K) + opaque(lh), rrn);
-          load_vec_nt<K>(histq(e) + g * (LPS * K) + opaque(lh), qrn);
+        // A step's inputs: the block's four recorded rows and the step's scalars, loaded one
+        // step ahead of the arithmetic into two register sets used in turn (as over_blocks).
+        struct CIn {
+          MT l[K], r[K];
+          float p[K], q[K];
+          float w, g, wh, xb;
+          double lz;
         };
-        rows_at(entry(t1 - 1));
-        for (long long t = t1 - 1; t >= t0; --t) {
-          MT lc[K], rr[K];
-          float pc[K], qr[K];
-#pragma unroll
-          for (int i = 0; i < K; ++i) {
-            lc[i] = lcn[i];
-            rr[i] = rrn[i];
-            pc[i] = pcn[i];
-            qr[i] = qrn[i];
-          }
-          rows_at(entry(t > t0 ? t - 1 : t));
-          const float u = k.sc * wb[t];
-          const float gt = gb[t];
-          const float gtp = gt * k.csc;
-          const float gwh = gt * whb[t];
-          const MT LZ = (MT)lzt[t];
-          const float hx = h - xbt[t];
-#pragma unroll
-          for (int r = 0; r < K; ++r) qr[r] -= gwh;
+        auto cload = [&](long long t, CIn& in) {
+          const long long e = entry(t);
+          load_vec_nt<K>(histl(e) + g * (LPS * K) + opaque(lh), in.l);
+          load_vec_nt<K>(histp(e) + g * (LPS * K) + opaque(lh), in.p);
+          load_vec_nt<K>(histr(e) + g * (LPS * K) + opaque(lh), in.r);
+          load_vec_nt<K>(histq(e) + g * (LPS * K) + opaque(lh), in.q);
+          in.w = wb[t];
+          in.g = gb[t];
+          in.wh = whb[t];
+          in.xb = xbt[t];
+          in.lz = lzt[t];
+        };
+        auto cstep = [&](const CIn& in) {
+          const float u = k.sc * in.w;
+          const float gt = in.g;
+          const float gwh = gt * in.wh;
+          const MT LZ = (MT)in.lz;
+          const float hx = h - in.xb;
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            const MT lz = lc[a] - LZ;
-            const float pa = pc[a] + hx;
+            const MT lz = in.l[a] - LZ;
+            const float pa = in.p[a] + hx;
 #pragma unroll
             for (int r = 0; r < K; ++r) {
-              const float v = Vg[r][a];
-              const float dd = u - v;
-              const float gm = ex2((float)(emit<P>(u, v, rr[r], k.kap) + lz));
-              const float eh = gm * (__builtin_fmaf(gtp, v, qr[r]) + pa);
+              const float c = Vg[a][r];
+              const float dd = sdiff<P>(u, k.sc, c);
+              const float gm = ex2((float)(emit_d<P>(dd, in.r[r], k.kap) + lz));
+              const float eh = gm * (__builtin_fmaf(gt, c, in.q[r] - gwh) + pa);
               ac[a][r] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd, eh, ac[a][r]));
             }
           }
+        };
+        CIn ca, cc;
+        cload(t1 - 1, ca);
+        for (long long t = t1 - 1;; t -= 2) {  // steps t and t - 1 (when t > t0)
+          cload(t > t0 ? t - 1 : t, cc);
+          cstep(ca);
+          if (t == t0) break;
+          cload(t - 1 > t0 ? t - 2 : t - 1, ca);
+          cstep(cc);
+          if (t - 1 == t0) break;
         }
 #pragma unroll
         for (int a = 0; a < K; ++a) {
