@@ -1,0 +1,162 @@
+"""Conventions of the C ABI that hold for every trellis kernel, beyond agreement with the oracle:
+- chains are independent: a NaN in one chain's weights reaches that chain's outputs and leaves
+  every other chain's outputs bitwise unchanged, including chains that share a wave or a
+  workspace slot with it (the codebook gradient, a sum over chains, is not compared);
+- calls made at once from several host threads, each on its own stream, give the serial
+  results bitwise."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+from bcjr_soft_decoding_amd import bcjr, synth
+from tests.gpu_helpers import dev, log_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bcjr.lib()
+
+
+def _inputs(n, B, L, seed):
+    rng = np.random.default_rng(seed)
+    c = rng.standard_normal(1 << n).astype(np.float32)
+    w = rng.standard_normal((B, L)).astype(np.float32)
+    g = rng.standard_normal((B, L)).astype(np.float32)
+    h = rng.standard_normal(B).astype(np.float32)
+    return c, w, g, h
+
+
+def _sparse(n, c, w, g, h, T, ckpt=False):
+    k = 2
+    B, L = w.shape
+    cd, wd = dev(c), dev(w)
+    wf = bcjr.workspace(n, k, B, L, bcjr.FWD_CKPT if ckpt else bcjr.FWD)
+    wb = bcjr.workspace(n, k, B, L, bcjr.BWD_CKPT if ckpt else bcjr.BWD)
+    w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, k, T, ws=wf)
+    gw, _ = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), dev(h), ws=wb)
+    states, w_hard = bcjr.viterbi_decode(cd, wd, n, k)
+    torch.cuda.synchronize()
+    return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard}
+
+
+def _check_isolated(clean, poisoned, j, what):
+    for key, a in clean.items():
+        a = a.cpu().numpy()
+        b = poisoned[key].cpu().numpy()
+        others = np.arange(a.shape[0]) != j
+        assert np.array_equal(a[others].view(np.uint8), b[others].view(np.uint8)), \
+            f"{what}: {key} of another chain changed"
+    assert np.isnan(poisoned["log_z"][j].item()), f"{what}: the NaN did not reach log Z"
+
+
+# (n, B, L, T, checkpointed history): chains that share a wave (S = 16, 256), one or two waves
+# per chain (S = 4096), 1024-lane chains with fp32 and fp64 messages
+CASES = [
+    (4, 70, 33, 0.3, False),
+    (8, 90, 40, 0.1, False),
+    (8, 90, 40, 0.1, True),
+    (12, 20, 30, 0.1, False),
+    (14, 5, 12, 0.005, False),
+    (16, 5, 10, 0.3, False),
+]
+
+
+@pytest.mark.parametrize("n,B,L,T,ckpt", CASES)
+def test_nan_stays_in_its_chain(n, B, L, T, ckpt):
+    log_case(f"NaN isolation n={n} B={B} L={L} T={T} ckpt={ckpt}")
+    c, w, g, h = _inputs(n, B, L, 100 + n)
+    clean = _sparse(n, c, w, g, h, T, ckpt)
+    j = B // 2 + 1
+    w2 = w.copy()
+    w2[j, L // 2] = np.nan
+    poisoned = _sparse(n, c, w2, g, h, T, ckpt)
+    _check_isolated(clean, poisoned, j, f"n={n}")
+    assert np.all(np.isnan(poisoned["w_hat"][j].cpu().numpy())), "NaN did not reach w_hat"
+
+
+def test_nan_stays_in_its_chain_segmented_and_dense():
+    n, B, L, T = 8, 40, 96, 0.1
+    log_case(f"NaN isolation, segmented n={n} B={B} L={L}")
+    c, w, g, _ = _inputs(n, B, L, 7)
+    j = 13
+    w2 = w.copy()
+    w2[j, 5] = np.nan
+    outs = []
+    for ww in (w, w2):
+        wh, lz = bcjr.bcjr_forward_scan(dev(c), dev(ww), n, 2, T, seg_len=16)
+        gw, _ = bcjr.bcjr_backward_scan(dev(c), dev(ww), n, 2, T, wh, dev(g), seg_len=16)
+        torch.cuda.synchronize()
+        outs.append({"w_hat": wh, "log_z": lz, "grad_w": gw})
+    _check_isolated(outs[0], outs[1], j, "segmented")
+
+    S, B, L, T = 64, 30, 20, 0.2
+    log_case(f"NaN isolation, dense S={S} B={B} L={L}")
+    rng = np.random.default_rng(9)
+    theta = rng.standard_normal((S, S)).astype(np.float32)
+    c = rng.standard_normal(S).astype(np.float32)
+    w = rng.standard_normal((B, L)).astype(np.float32)
+    g = rng.standard_normal((B, L)).astype(np.float32)
+    w2 = w.copy()
+    w2[j, 3] = np.nan
+    outs = []
+    for ww in (w, w2):
+        wh, lz, saved = bcjr.bcjr_dense_forward(dev(theta), dev(c), dev(ww), T)
+        gw, _, _ = bcjr.bcjr_dense_backward(dev(theta), dev(c), dev(ww), T, saved, dev(g))
+        torch.cuda.synchronize()
+        outs.append({"w_hat": wh, "log_z": lz, "grad_w": gw})
+    _check_isolated(outs[0], outs[1], j, "dense")
+
+
+def test_threads_on_their_own_streams_match_serial():
+    """Two host threads, each issuing forward, backward and Viterbi calls on its own stream
+    (default priority) four times over, while the other does the same."""
+    jobs = [(12, 300, 64, 0.1, 1), (8, 3000, 128, 0.3, 2)]
+    inputs = [_inputs(n, B, L, seed) for n, B, L, _, seed in jobs]
+    log_case("threads: serial reference")
+    ref = [_sparse(n, *inp, T) for (n, _, _, T, _), inp in zip(jobs, inputs)]
+    results = [[] for _ in jobs]
+    errors = []
+
+    def work(i):
+        try:
+            n, _, _, T, _ = jobs[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(4):
+                    out = _sparse_on_stream(n, *inputs[i], T)
+                    results[i].append(out)
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    log_case("threads: two concurrent workers")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    for i, runs in enumerate(results):
+        assert len(runs) == 4
+        for out in runs:
+            for key, a in ref[i].items():
+                assert np.array_equal(a.cpu().numpy().view(np.uint8),
+                                      out[key].cpu().numpy().view(np.uint8)), (i, key)
+
+
+def _sparse_on_stream(n, c, w, g, h, T):
+    """As _sparse, synchronising only the current stream (the other worker keeps running)."""
+    k = 2
+    B, L = w.shape
+    cd, wd = dev(c), dev(w)
+    w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, k, T)
+    gw, _ = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), dev(h))
+    states, w_hard = bcjr.viterbi_decode(cd, wd, n, k)
+    torch.cuda.current_stream().synchronize()
+    return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard}
