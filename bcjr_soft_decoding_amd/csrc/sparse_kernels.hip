@@ -712,8 +712,9 @@ __device__ __forceinline__ void pin(T& x) {
 // values and intermediates, so the G blocks are visited in a rolled loop: a block's column
 // offsets are read from LDS when it is processed, its outputs go straight to the other message
 // buffer (one buffer per step parity), and the codebook values and history entries of the next
-// block are loaded while the current one is computed. The per-block arithmetic and the history
-// layout are those of k_sparse_fwd (mode 0).
+// block are loaded while the current one is computed, into the other of two register sets
+// (over_blocks). The per-block arithmetic and the history layout are those of k_sparse_fwd
+// (mode 0).
 // ---------------------------------------------------------------------------------------------
 template <class C, bool CK>
 __global__ void __launch_bounds__(C::BLOCK)
@@ -1450,8 +1451,8 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   const unsigned lo4 = K * p;
   float* __restrict__ accs = partial + (size_t)blockIdx.x * C::S;
   auto col = [](int g, int a) { return g * K * LPS + a * M; };
-  // the block's raw codebook values c[a][r] (scaled where used, so that a load issued a block
-  // ahead is not waited for at once)
+  // the block's raw codebook values c[a][r]; the scaled differences u - sc * c are formed
+  // from them where used (sdiff), so a load issued a block ahead is not waited for at once
   auto cblock = [&](int g, float (&c)[K][K]) {
 #pragma unroll
     for (int a = 0; a < K; ++a) {
