@@ -32,6 +32,9 @@
  *     synchronise. A launch failure is reported as BCJR_E_DEVICE by the call that sees it.
  *   - Inputs are not checked for NaN or Inf: the forward-backward entry points assume finite
  *     w, codebook and theta (NaN gives unspecified outputs); the Viterbi decoder is IEEE-exact.
+ *     Chains are independent: a NaN or Inf in one chain's weights leaves every other chain's
+ *     w_hat, log_z, grad_w and decoded path unchanged (it reaches the gradients that sum over
+ *     chains: the codebook's and theta's).
  *   - Results are bitwise deterministic for a given device, input and argument set.
  *   - The library is thread safe (no shared mutable state); use one stream per thread.
  */
