@@ -1027,6 +1027,9 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
   const int q = LPS < 64 ? tid / LPS : 0;
   const int p = LPS < 64 ? tid % LPS : tid;
   const float k2 = 2.0f * k.inv_t * k.csc;  // (2/T)(w - c) = k2 * (u - v)
+  // The codebook-gradient sums are carried divided by k2 (one multiply fewer per state and
+  // step): acc = sum_t [(g_t / k2) gamma + (u - v) E], times k2 when the partials are written.
+  const float ik2 = 1.0f / k2;
 
   CodebookLane<C> vsrc;
   vsrc.init(cb, k.sc, p);
@@ -1299,6 +1302,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         const float u = k.sc * wb[t];
         const float gt = gb[t];
         const float gtp = gt * k.csc;
+        const float gtk = gt * ik2;
         const float gwh = gt * whb[t];
         const MT LZ = (MT)((lz2 - Nt) - Np);
         float qrc[G][K];  // Psi_t - g_t w_hat_t at the row offsets
@@ -1354,7 +1358,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
                 const float gm = e[r] * f;
                 const float eh = gm * (t2[r] + pa);
                 gw = __builtin_fmaf(Vg[r][a], eh, gw);
-                acc[g][r][a] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd[r], eh, acc[g][r][a]));
+                acc[g][r][a] = __builtin_fmaf(gtk, gm, __builtin_fmaf(dd[r], eh, acc[g][r][a]));
               }
             }
           }
@@ -1406,7 +1410,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
           for (int o = LPS; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
         }
-        if (q == 0) partial[(size_t)blockIdx.x * C::S + K * (p + g * LPS) + r + a * M] = v;
+        if (q == 0) partial[(size_t)blockIdx.x * C::S + K * (p + g * LPS) + r + a * M] = k2 * v;
       }
 }
 
