@@ -14,15 +14,17 @@
 namespace bcjr {
 
 // kFwd / kBwd: forward and backward with fp32 messages; kFwdP / kBwdP: the same kernels with
-// fp64 messages (twice the message registers, so fewer states per lane); kVit: Viterbi.
-enum Kind { kFwd = 0, kBwd = 1, kVit = 2, kFwdP = 3, kBwdP = 4 };
+// fp64 messages (twice the message registers, so fewer states per lane); kVit: Viterbi;
+// kFwdS / kBwdS: the fp32 kernels over the segments of the segmented (parallel-in-L) path, which
+// has few chains in flight, so it spreads each over more lanes.
+enum Kind { kFwd = 0, kBwd = 1, kVit = 2, kFwdP = 3, kBwdP = 4, kFwdS = 5, kBwdS = 6 };
 
 constexpr int kMaxLanesPerChain = 1024;
 
 // States per lane each kernel aims for (more states per lane: fewer lanes per chain, cheaper
 // per-step exchanges and reductions, more registers). Measured on MI355X at S = 4096.
 constexpr int geom_target_states(int kind) {
-  return kind == kFwd ? 64 : kind == kBwd ? 32 : kind == kFwdP ? 32 : 16;
+  return kind == kFwd ? 64 : kind == kBwd ? 32 : kind == kFwdP ? 32 : 16;  // kBwdP, kVit, kFwdS, kBwdS: 16
 }
 
 // Kernels are built for k in {1, 2, 3} and 2k <= n <= 16, except where the two backward
@@ -57,5 +59,6 @@ static_assert(geom_g(12, 2, kBwd) == 2 && geom_lps(12, 2, kBwd) == 128, "S=4096 
 static_assert(geom_g(16, 2, kBwd) == 4 && geom_lps(16, 2, kBwd) == 1024, "S=65536 geometry");
 static_assert(geom_g(4, 2, kFwd) == 1 && geom_lps(4, 2, kFwd) == 1, "S=16 geometry");
 static_assert(geom_g(8, 2, kBwd) == 2 && geom_lps(8, 2, kBwd) == 8, "S=256 geometry");
+static_assert(geom_g(8, 2, kFwdS) == 1 && geom_lps(8, 2, kBwdS) == 16, "S=256 segment geometry");
 
 }  // namespace bcjr

@@ -142,8 +142,10 @@ bcjr_status scan_setup(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg
   const int64_t pmain = L / s_eff;
   const int64_t ptot = pmain + (L % s_eff ? 1 : 0);
   if (B > 0 && ptot > ((int64_t)1 << 58) / (B * M * M * 4)) return BCJR_E_SHAPE;
+  // the segments run with the segment geometry (fp32 messages) or the fp64 one; the plan's
+  // history sizes take the larger of the two (sparse_fwd_ws_bytes)
   SparseGeom gm, gt;
-  if (!sparse_geom(n, k, B * pmain, kFwd, &gm) || !sparse_geom(n, k, B, kFwd, &gt))
+  if (!sparse_geom(n, k, B * pmain, kFwdS, &gm) || !sparse_geom(n, k, B, kFwdS, &gt))
     return BCJR_E_UNSUPPORTED;
   scan_plan(gm, gt, n, k, B, L, seg, plan);
   return BCJR_OK;
@@ -157,7 +159,7 @@ bcjr_status scan_setup_bwd(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t
   if (st != BCJR_OK) return st;
   const int n = tr->state_bits, k = tr->bits_per_step;
   SparseGeom gm, gt, pm, pt;
-  if (!sparse_geom(n, k, B * f.pmain, kBwd, &gm) || !sparse_geom(n, k, B, kBwd, &gt) ||
+  if (!sparse_geom(n, k, B * f.pmain, kBwdS, &gm) || !sparse_geom(n, k, B, kBwdS, &gt) ||
       !sparse_geom(n, k, B * f.pmain, kBwdP, &pm) || !sparse_geom(n, k, B, kBwdP, &pt))
     return BCJR_E_UNSUPPORTED;
   const int64_t slots = (gm.slots > pm.slots ? gm.slots : pm.slots) +

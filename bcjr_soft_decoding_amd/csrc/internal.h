@@ -137,16 +137,17 @@ constexpr int64_t kScanMinSeg = 16;
 
 // Default segment length. A chain's time is about P * t2 (the boundary scan, sequential over
 // its P = L / seg segments) + seg * t3 (each segment's own sweeps, sequential in its steps),
-// smallest at seg = sqrt(L * t2 / t3). Measured on MI355X: t3 = 3.0 us per step (forward and
-// backward sweep of one chain); per scan step t2 = 1.0 us + 0.03 us * M for M = S/K <= 64
-// (one wave per chain and direction) and 2.5 us + 3.7e-4 us * M^2 above (one block).
+// smallest at seg = sqrt(L * t2 / t3). Measured on MI355X: t3 = 1.5 us per step (forward and
+// backward sweep of one chain, with the segment geometry kFwdS / kBwdS); per scan step
+// t2 = 1.0 us + 0.03 us * M for M = S/K <= 64 (one wave per chain and direction) and
+// 2.5 us + 3.7e-4 us * M^2 above (one block).
 // A segment shorter than the others (when seg does not divide L) runs in launches of its own
 // after the others, so the default prefers a divisor of L within 1.5x of that optimum, else
 // seg = floor(L / P) for P = ceil(L / optimum), which keeps the short segment under P steps.
 inline int64_t scan_default_seg(int n, int k, int64_t B, int64_t L) {
   (void)B;
   const double M = (double)(((int64_t)1 << n) >> k);
-  const double t2 = M <= 64 ? 1.0 + 0.03 * M : 2.5 + 3.7e-4 * M * M, t3 = 3.0;
+  const double t2 = M <= 64 ? 1.0 + 0.03 * M : 2.5 + 3.7e-4 * M * M, t3 = 1.5;
   const double opt = sqrt((double)L * t2 / t3);
   if (opt <= (double)kScanMinSeg) return kScanMinSeg;
   if (opt >= (double)L) return L;

@@ -1949,6 +1949,11 @@ template <class P>
 constexpr int fwd_kind() { return P::kPrecise ? kFwdP : kFwd; }
 template <class P>
 constexpr int bwd_kind() { return P::kPrecise ? kBwdP : kBwd; }
+// the segments of the segmented path (boundary mode 1): few chains, more lanes each
+template <class P, int BM>
+constexpr int fwd_seg_kind() { return BM == 1 && !P::kPrecise ? kFwdS : fwd_kind<P>(); }
+template <class P, int BM>
+constexpr int bwd_seg_kind() { return BM == 1 && !P::kPrecise ? kBwdS : bwd_kind<P>(); }
 template <int n, int k>
 bool use_precise(float T) {
   return precise_fits<n, k>() && T < kPreciseBelowT;
@@ -2092,8 +2097,9 @@ template <int n, int k, class P, int BM>
 int run_fwd_seg_p(const float* cb, const float* w, long long Bv, long long L, float T,
                   float* w_hat, float* log_z, void* ws, const SegArgs& sa, hipStream_t st) {
   SparseGeom g;
-  if (!sparse_geom(n, k, Bv, fwd_kind<P>(), &g)) return (int)hipErrorInvalidValue;
-  using C = Cfg<(1 << k), geom_g(n, k, fwd_kind<P>()), geom_lps(n, k, fwd_kind<P>()), P, false>;
+  constexpr int kind = fwd_seg_kind<P, BM>();
+  if (!sparse_geom(n, k, Bv, kind, &g)) return (int)hipErrorInvalidValue;
+  using C = Cfg<(1 << k), geom_g(n, k, kind), geom_lps(n, k, kind), P, false>;
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
   const Consts kc = make_consts(T, P::kPrecise);
   const size_t slot = BM == 2 ? 0 : sparse_fwd_slot_bytes(g, L, false);
@@ -2123,8 +2129,9 @@ int run_bwd_seg_p(const float* cb, const float* w, long long Bv, long long L, fl
                   const float* w_hat, const float* gup, const float* hup, float* grad_w,
                   float* partial, void* ws, const SegArgs& sa, int* grid_used, hipStream_t st) {
   SparseGeom g;
-  if (!sparse_geom(n, k, Bv, bwd_kind<P>(), &g)) return (int)hipErrorInvalidValue;
-  using C = Cfg<(1 << k), geom_g(n, k, bwd_kind<P>()), geom_lps(n, k, bwd_kind<P>()), P, true>;
+  constexpr int kind = bwd_seg_kind<P, BM>();
+  if (!sparse_geom(n, k, Bv, kind, &g)) return (int)hipErrorInvalidValue;
+  using C = Cfg<(1 << k), geom_g(n, k, kind), geom_lps(n, k, kind), P, true>;
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
   const Consts kc = make_consts(T, P::kPrecise);
   const size_t slot = BM == 2 ? 0 : sparse_bwd_slot_bytes(g, L, false);
