@@ -3,7 +3,8 @@
   every other chain's outputs bitwise unchanged, including chains that share a wave or a
   workspace slot with it (the codebook gradient, a sum over chains, is not compared);
 - calls made at once from several host threads, each on its own stream, give the serial
-  results bitwise."""
+  results bitwise;
+- with no chains the codebook gradient (a sum over none) is written as zeros."""
 import threading
 
 import numpy as np
@@ -160,3 +161,24 @@ def _sparse_on_stream(n, c, w, g, h, T):
     states, w_hard = bcjr.viterbi_decode(cd, wd, n, k)
     torch.cuda.current_stream().synchronize()
     return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard}
+
+
+@pytest.mark.parametrize("n,T,ckpt", [(8, 0.5, False), (8, 0.5, True), (15, 0.005, False),
+                                      (16, 0.3, False), (16, 0.3, True)])
+def test_zero_chains_overwrite_the_codebook_gradient(n, T, ckpt):
+    """B = 0: the codebook gradient (a sum over no chains) is written as zeros over a
+    NaN-filled buffer, and the other outputs are empty."""
+    log_case(f"B=0 n={n} T={T} ckpt={ckpt}")
+    k, L = 2, 9
+    c = dev(synth.normal(40 + n, (1 << n,)))
+    w = torch.empty((0, L), dtype=torch.float32, device="cuda")
+    wf = bcjr.workspace(n, k, 0, L, bcjr.FWD_CKPT if ckpt else bcjr.FWD)
+    wb = bcjr.workspace(n, k, 0, L, bcjr.BWD_CKPT if ckpt else bcjr.BWD)
+    w_hat, log_z, saved = bcjr.bcjr_forward(c, w, n, k, T, ws=wf)
+    gc = torch.full((1 << n,), float("nan"), dtype=torch.float32, device="cuda")
+    gw, gc2 = bcjr.bcjr_backward(c, w, n, k, T, saved, torch.empty_like(w), grad_codebook=gc, ws=wb)
+    states, w_hard = bcjr.viterbi_decode(c, w, n, k)
+    torch.cuda.synchronize()
+    assert w_hat.numel() == 0 and log_z.numel() == 0 and gw.numel() == 0 and states.numel() == 0
+    assert gc2.data_ptr() == gc.data_ptr()
+    assert torch.count_nonzero(gc).item() == 0 and not torch.isnan(gc).any().item()
