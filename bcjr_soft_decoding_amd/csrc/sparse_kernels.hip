@@ -606,9 +606,11 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
           for (int a = 0; a < K; ++a) lcur[g][a] = lcn[g][a];
         const double Nt = Nn;
-        if (t > t0) {
-          load_vec<KG>(hist(entry(t - 1)), &lcn[0][0]);
-          Nn = ns[(t - 1) * SPB + q];
+        {  // unconditional (at the segment's first step it re-reads step t): a conditional load
+           // makes the compiler copy the carried rows out and back every step
+          const long long tp = t > t0 ? t - 1 : t;
+          load_vec<KG>(hist(entry(tp)), &lcn[0][0]);
+          Nn = ns[tp * SPB + q];
         }
         const float u = k.sc * wb[t];
         const MT LZ = (MT)((lz2 - Nt) - Np);
@@ -1294,10 +1296,12 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
           for (int a = 0; a < K; ++a) { lcur[g][a] = lcn[g][a]; pcur[g][a] = pcn[g][a]; }
         const double Nt = Nn;
-        if (t > t0) {
-          load_vec<KG>(histl(entry(t - 1)), &lcn[0][0]);
-          load_vec<KG>(histp(entry(t - 1)), &pcn[0][0]);
-          Nn = ns[(t - 1) * SPB + q];
+        {  // unconditional (at the segment's first step it re-reads step t): a conditional load
+           // makes the compiler copy the carried rows out and back every step
+          const long long tp = t > t0 ? t - 1 : t;
+          load_vec<KG>(histl(entry(tp)), &lcn[0][0]);
+          load_vec<KG>(histp(entry(tp)), &pcn[0][0]);
+          Nn = ns[tp * SPB + q];
         }
         const float u = k.sc * wb[t];
         const float gt = gb[t];
