@@ -118,6 +118,9 @@ bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int6
  * grad_codebook DEVICE [S] written (overwritten, summed over all B chains, fixed-order sum)
  * ws         DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 4) (checkpointed history) or
  *            >= bcjr_workspace_bytes(tr, B, L, 1) (full history)
+ * Precision: messages are fp64 below T = 0.01 and fp32 above, except at S = 2^16, where they are
+ * fp32 at every T (fp64 would not fit LDS); there, below T = 0.01, grad_w can lose accuracy
+ * beyond 1e-3 on inputs whose paths nearly tie (w_hat, log_z and grad_codebook do not).
  */
 bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                           const void* saved, const float* grad_w_hat, const float* grad_log_z,
