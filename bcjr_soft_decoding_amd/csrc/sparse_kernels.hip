@@ -80,14 +80,21 @@ struct Consts {
   float inv_t;  // 1/T
 };
 
+// With fp64 messages the difference w - c is itself formed in fp64 (exactly: both are fp32);
+// rounded to fp32 it would move the emission by ~kappa (w - c)^2 * 2^-23, which at small T is
+// enough to shift near-tied posteriors.
 template <class P>
 __device__ __forceinline__ typename P::MT emit(float u, float v, typename P::MT off, double kap) {
-  const float d = u - v;
   if constexpr (P::kPrecise) {
-    const double dd = (double)d;
+    // (converted at each use: hoisted out of the step loop, the fp64 codebook values would
+    // take twice the registers of the fp32 ones)
+    float vv = v;
+    asm volatile("" : "+v"(vv));
+    const double dd = (double)u - (double)vv;
     return __builtin_fma(-(kap * dd), dd, off);
   } else {
     (void)kap;
+    const float d = u - v;
     return __builtin_fmaf(-d, d, off);
   }
 }
@@ -102,13 +109,17 @@ __device__ __forceinline__ float sdiff(float u, float sc, float c) {
     return __builtin_fmaf(-sc, c, u);
   }
 }
+// The emission from a raw codebook value: emit(u, sc * c) with the fp32 difference as one fma
+// (with fp64 messages sc = 1 and the difference is formed in fp64, as in emit).
 template <class P>
-__device__ __forceinline__ typename P::MT emit_d(float d, typename P::MT off, double kap) {
+__device__ __forceinline__ typename P::MT emit_c(float u, float sc, float c, typename P::MT off,
+                                                 double kap) {
   if constexpr (P::kPrecise) {
-    const double dd = (double)d;
-    return __builtin_fma(-(kap * dd), dd, off);
+    (void)sc;
+    return emit<P>(u, c, off, kap);
   } else {
     (void)kap;
+    const float d = __builtin_fmaf(-sc, c, u);
     return __builtin_fmaf(-d, d, off);
   }
 }
@@ -811,7 +822,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
               MT m = (MT)-INFINITY;
 #pragma unroll
               for (int a = 0; a < K; ++a) {
-                x[a] = emit_d<P>(sdiff<P>(u, k.sc, in.c[a][r]), lc[a], k.kap);
+                x[a] = emit_c<P>(u, k.sc, in.c[a][r], lc[a], k.kap);
                 m = tmax(m, x[a]);
               }
               float s = ex2((float)(x[0] - m));
@@ -942,7 +953,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
                 MT m = (MT)-INFINITY;
 #pragma unroll
                 for (int r = 0; r < K; ++r) {
-                  y[r] = emit_d<P>(sdiff<P>(u, k.sc, in.c[a][r]), rr[r], k.kap);
+                  y[r] = emit_c<P>(u, k.sc, in.c[a][r], rr[r], k.kap);
                   m = tmax(m, y[r]);
                 }
                 // cw: the column's weighted sum of raw codebook values
@@ -1588,7 +1599,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
           MT m = (MT)-INFINITY;
 #pragma unroll
           for (int a = 0; a < K; ++a) {
-            x[a] = emit_d<P>(sdiff<P>(u, k.sc, Vg[a][r]), lc[a], k.kap);
+            x[a] = emit_c<P>(u, k.sc, Vg[a][r], lc[a], k.kap);
             m = tmax(m, x[a]);
           }
           float e0 = ex2((float)(x[0] - m));
@@ -1809,7 +1820,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             MT m = (MT)-INFINITY;
 #pragma unroll
             for (int r = 0; r < K; ++r) {
-              y[r] = emit_d<P>(sdiff<P>(u, k.sc, V[r]), rr[r], k.kap);
+              y[r] = emit_c<P>(u, k.sc, V[r], rr[r], k.kap);
               m = tmax(m, y[r]);
             }
             float e4[K], t2[K];
@@ -1904,7 +1915,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             for (int r = 0; r < K; ++r) {
               const float c = Vg[a][r];
               const float dd = sdiff<P>(u, k.sc, c);
-              const float gm = ex2((float)(emit_d<P>(dd, in.r[r], k.kap) + lz));
+              const float gm = ex2((float)(emit_c<P>(u, k.sc, c, in.r[r], k.kap) + lz));
               const float eh = gm * (__builtin_fmaf(gt, c, in.q[r] - gwh) + pa);
               ac[a][r] = __builtin_fmaf(gt, gm, __builtin_fmaf(k2 * dd, eh, ac[a][r]));
             }

@@ -190,3 +190,26 @@ def test_bitwise_deterministic_and_poisoned_workspace():
     for a, b in zip(*outs):
         assert np.all(np.isfinite(a))
         np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_fp64_messages_form_the_emission_difference_exactly():
+    """S=32 at T=0.004 (fp64 messages, checkpointed history) on inputs with near-tied posteriors:
+    with w - c rounded to fp32 before the fp64 emission, w_hat erred by 1.6e-4 normwise here."""
+    n, B, L, T = 5, 215, 189, 0.004
+    r = np.random.default_rng(251723242)
+    c = r.standard_normal(1 << n).astype(np.float32)
+    w = (r.standard_normal((B, L)) * r.choice([0.3, 1.0, 2.0])).astype(np.float32)
+    g = r.standard_normal((B, L)).astype(np.float32)
+    log_case(f"fp64 emission n={n} B={B} L={L} T={T}")
+    ref = oracle.sparse_forward(n, 2, c, w, T)
+    rb = oracle.sparse_backward(n, 2, c, w, T, g)
+    cd, wd = dev(c), dev(w)
+    wf = bcjr.workspace(n, 2, B, L, bcjr.FWD_CKPT)
+    wb = bcjr.workspace(n, 2, B, L, bcjr.BWD_CKPT)
+    w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, 2, T, ws=wf)
+    gw, gc = bcjr.bcjr_backward(cd, wd, n, 2, T, saved, dev(g), ws=wb)
+    torch.cuda.synchronize()
+    assert_normwise(w_hat.cpu().numpy(), ref["w_hat"], RTOL_FWD, "w_hat")
+    assert_rel(log_z.cpu().numpy(), ref["log_z"], RTOL_FWD, "log_z")
+    assert_normwise(gw.cpu().numpy(), rb["grad_w"], RTOL_GRAD, "grad_w")
+    assert_normwise(gc.cpu().numpy(), rb["grad_codebook"], RTOL_GRAD, "grad_c")
