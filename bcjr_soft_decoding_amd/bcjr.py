@@ -12,8 +12,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# BCJR_LIB may point at another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("BCJR_LIB", os.path.join(_PKG, "_lib", "libbcjr.so"))
+LIB_PATH = os.path.join(_PKG, "_lib", "libbcjr.so")
 
 BCJR_OK, BCJR_E_ARG, BCJR_E_SHAPE, BCJR_E_WORKSPACE, BCJR_E_DEVICE, BCJR_E_UNSUPPORTED = range(6)
 FWD, BWD, VIT, FWD_CKPT, BWD_CKPT = 0, 1, 2, 3, 4
@@ -109,8 +108,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def trellis(n: int, k: int, codebook=None, v: int = 1) -> Trellis:
@@ -122,10 +121,68 @@ def _check(st: int, what: str):
         raise BcjrError(st, what)
 
 
-def _f32(t, name):
-    if not (t.dtype == torch.float32 and t.is_cuda and t.is_contiguous()):
-        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
-    return t
+# ---- argument checks -----------------------------------------------------------------------
+# The C ABI receives raw pointers and cannot see a tensor's extent, so every tensor is checked
+# here against the sizes the call implies before anything is passed down: a short codebook or
+# output would otherwise be read or written past its end on the device. Shapes and dtypes are
+# checked first, then that every tensor is a CUDA tensor on one device; nothing is allocated
+# or launched before both pass.
+
+F32, I32, U32 = torch.float32, torch.int32, torch.uint32
+
+
+def _spec(t, name, dtype, shape):
+    """t (None = not given) must be a contiguous tensor of this dtype and exact shape."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(s) for s in shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _spec_bytes(t, name, need, align=16):
+    """A byte buffer of any dtype (None = not given) holding at least `need` bytes; returns its
+    size in bytes."""
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < need:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {need}")
+    if t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
+    return have
+
+
+def _chains2(t, name, dtype=F32):
+    """The [B, L] array that fixes a call's shape; returns (B, L)."""
+    _spec(t, name, dtype, None)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must have shape [B, L], got {tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _device(*tensors):
+    """Every given tensor must be a CUDA tensor, all on one device; returns that device."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"expected CUDA tensors, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on {dev} and {t.device}: a call runs on one device")
+    return dev
 
 
 def bcjr_supported(n: int, k: int, v: int = 1) -> bool:
@@ -151,18 +208,26 @@ def workspace(n, k, B, L, which, device="cuda"):
 
 def bcjr_forward(codebook, w, n, k, T, w_hat=None, log_z=None, saved=None, ws=None):
     """Soft codeword w_hat [B,L] and log Z [B]; returns (w_hat, log_z, saved)."""
-    _f32(codebook, "codebook"); _f32(w, "w")
-    B, L = w.shape
-    dev = w.device
+    B, L = _chains2(w, "w")
+    S = 1 << int(n)
+    _spec(codebook, "codebook", F32, (S,))
+    _spec(w_hat, "w_hat", F32, (B, L))
+    _spec(log_z, "log_z", F32, (B,))
+    need_saved = bcjr_saved_bytes(n, k, B, L)
+    _spec_bytes(saved, "saved", need_saved)
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, w_hat, log_z, saved, ws)
     w_hat = torch.empty_like(w) if w_hat is None else w_hat
-    log_z = torch.empty(B, dtype=torch.float32, device=dev) if log_z is None else log_z
+    log_z = torch.empty(B, dtype=F32, device=dev) if log_z is None else log_z
     if saved is None:
-        saved = torch.empty(max(bcjr_saved_bytes(n, k, B, L), 1), dtype=torch.uint8, device=dev)
+        saved = torch.empty(max(need_saved, 1), dtype=torch.uint8, device=dev)
     if ws is None:
         ws = workspace(n, k, B, L, FWD, dev)
     tr = trellis(n, k, codebook)
-    st = lib().bcjr_forward(ctypes.byref(tr), _ptr(w), B, L, float(T), _ptr(w_hat), _ptr(log_z),
-                            _ptr(saved), _ptr(ws), ws.numel(), _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_forward(ctypes.byref(tr), _ptr(w), B, L, float(T), _ptr(w_hat),
+                                _ptr(log_z), _ptr(saved), _ptr(ws), _spec_bytes(ws, "ws", 0),
+                                _stream(dev))
     _check(st, "bcjr_forward")
     return w_hat, log_z, saved
 
@@ -179,17 +244,22 @@ def bcjr_scan_workspace_bytes(n: int, k: int, B: int, L: int, seg_len: int = 0) 
 
 def bcjr_forward_scan(codebook, w, n, k, T, seg_len=0, w_hat=None, log_z=None, ws=None):
     """Segmented (parallel-in-L) forward for few, long chains; returns (w_hat, log_z)."""
-    _f32(codebook, "codebook"); _f32(w, "w")
-    B, L = w.shape
-    dev = w.device
+    B, L = _chains2(w, "w")
+    _spec(codebook, "codebook", F32, (1 << int(n),))
+    _spec(w_hat, "w_hat", F32, (B, L))
+    _spec(log_z, "log_z", F32, (B,))
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, w_hat, log_z, ws)
     w_hat = torch.empty_like(w) if w_hat is None else w_hat
-    log_z = torch.empty(B, dtype=torch.float32, device=dev) if log_z is None else log_z
+    log_z = torch.empty(B, dtype=F32, device=dev) if log_z is None else log_z
     if ws is None:
         nb = bcjr_scan_workspace_bytes(n, k, B, L, seg_len)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     tr = trellis(n, k, codebook)
-    st = lib().bcjr_forward_scan(ctypes.byref(tr), _ptr(w), B, L, float(T), int(seg_len),
-                                 _ptr(w_hat), _ptr(log_z), _ptr(ws), ws.numel(), _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_forward_scan(ctypes.byref(tr), _ptr(w), B, L, float(T), int(seg_len),
+                                     _ptr(w_hat), _ptr(log_z), _ptr(ws), _spec_bytes(ws, "ws", 0),
+                                     _stream(dev))
     _check(st, "bcjr_forward_scan")
     return w_hat, log_z
 
@@ -202,18 +272,27 @@ def bcjr_scan_backward_workspace_bytes(n: int, k: int, B: int, L: int, seg_len: 
 def bcjr_backward_scan(codebook, w, n, k, T, w_hat, grad_w_hat, grad_log_z=None, seg_len=0,
                        grad_w=None, grad_codebook=None, ws=None):
     """Segmented (parallel-in-L) backward; returns (grad_w, grad_codebook)."""
-    _f32(codebook, "codebook"); _f32(w, "w"); _f32(w_hat, "w_hat"); _f32(grad_w_hat, "grad_w_hat")
-    B, L = w.shape
-    dev = w.device
+    B, L = _chains2(w, "w")
+    S = 1 << int(n)
+    _spec(codebook, "codebook", F32, (S,))
+    _spec(w_hat, "w_hat", F32, (B, L))
+    _spec(grad_w_hat, "grad_w_hat", F32, (B, L))
+    _spec(grad_log_z, "grad_log_z", F32, (B,))
+    _spec(grad_w, "grad_w", F32, (B, L))
+    _spec(grad_codebook, "grad_codebook", F32, (S,))
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, w_hat, grad_w_hat, grad_log_z, grad_w, grad_codebook, ws)
     grad_w = torch.empty_like(w) if grad_w is None else grad_w
     grad_codebook = torch.empty_like(codebook) if grad_codebook is None else grad_codebook
     if ws is None:
         nb = bcjr_scan_backward_workspace_bytes(n, k, B, L, seg_len)
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     tr = trellis(n, k, codebook)
-    st = lib().bcjr_backward_scan(ctypes.byref(tr), _ptr(w), B, L, float(T), int(seg_len),
-                                  _ptr(w_hat), _ptr(grad_w_hat), _ptr(grad_log_z), _ptr(grad_w),
-                                  _ptr(grad_codebook), _ptr(ws), ws.numel(), _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_backward_scan(ctypes.byref(tr), _ptr(w), B, L, float(T), int(seg_len),
+                                      _ptr(w_hat), _ptr(grad_w_hat), _ptr(grad_log_z),
+                                      _ptr(grad_w), _ptr(grad_codebook), _ptr(ws),
+                                      _spec_bytes(ws, "ws", 0), _stream(dev))
     _check(st, "bcjr_backward_scan")
     return grad_w, grad_codebook
 
@@ -221,36 +300,49 @@ def bcjr_backward_scan(codebook, w, n, k, T, w_hat, grad_w_hat, grad_log_z=None,
 def bcjr_backward(codebook, w, n, k, T, saved, grad_w_hat, grad_log_z=None, grad_w=None,
                   grad_codebook=None, ws=None):
     """Gradient of sum(g * w_hat) + sum(h * log_z); returns (grad_w, grad_codebook)."""
-    _f32(codebook, "codebook"); _f32(w, "w"); _f32(grad_w_hat, "grad_w_hat")
-    if grad_log_z is not None:
-        _f32(grad_log_z, "grad_log_z")
-    B, L = w.shape
-    dev = w.device
+    B, L = _chains2(w, "w")
+    S = 1 << int(n)
+    _spec(codebook, "codebook", F32, (S,))
+    if saved is None:
+        raise ValueError("saved (the forward's context) is required")
+    _spec_bytes(saved, "saved", bcjr_saved_bytes(n, k, B, L))
+    _spec(grad_w_hat, "grad_w_hat", F32, (B, L))
+    _spec(grad_log_z, "grad_log_z", F32, (B,))
+    _spec(grad_w, "grad_w", F32, (B, L))
+    _spec(grad_codebook, "grad_codebook", F32, (S,))
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, saved, grad_w_hat, grad_log_z, grad_w, grad_codebook, ws)
     grad_w = torch.empty_like(w) if grad_w is None else grad_w
     grad_codebook = torch.empty_like(codebook) if grad_codebook is None else grad_codebook
     if ws is None:
         ws = workspace(n, k, B, L, BWD, dev)
     tr = trellis(n, k, codebook)
-    st = lib().bcjr_backward(ctypes.byref(tr), _ptr(w), B, L, float(T), _ptr(saved),
-                             _ptr(grad_w_hat), _ptr(grad_log_z), _ptr(grad_w),
-                             _ptr(grad_codebook), _ptr(ws), ws.numel(), _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_backward(ctypes.byref(tr), _ptr(w), B, L, float(T), _ptr(saved),
+                                 _ptr(grad_w_hat), _ptr(grad_log_z), _ptr(grad_w),
+                                 _ptr(grad_codebook), _ptr(ws), _spec_bytes(ws, "ws", 0),
+                                 _stream(dev))
     _check(st, "bcjr_backward")
     return grad_w, grad_codebook
 
 
 def viterbi_decode(codebook, w, n, k, states=None, w_hard=None, want_w_hard=True, ws=None):
     """Hard decode (the T -> 0 limit); returns (states int32 [B,L], w_hard [B,L] or None)."""
-    _f32(codebook, "codebook"); _f32(w, "w")
-    B, L = w.shape
-    dev = w.device
-    states = torch.empty((B, L), dtype=torch.int32, device=dev) if states is None else states
-    if want_w_hard and w_hard is None:
+    B, L = _chains2(w, "w")
+    _spec(codebook, "codebook", F32, (1 << int(n),))
+    _spec(states, "states", I32, (B, L))
+    _spec(w_hard, "w_hard", F32, (B, L))
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, states, w_hard, ws)
+    states = torch.empty((B, L), dtype=I32, device=dev) if states is None else states
+    if w_hard is None and want_w_hard:
         w_hard = torch.empty_like(w)
     if ws is None:
         ws = workspace(n, k, B, L, VIT, dev)
     tr = trellis(n, k, codebook)
-    st = lib().viterbi_decode(ctypes.byref(tr), _ptr(w), B, L, _ptr(states), _ptr(w_hard),
-                              _ptr(ws), ws.numel(), _stream())
+    with torch.cuda.device(dev):
+        st = lib().viterbi_decode(ctypes.byref(tr), _ptr(w), B, L, _ptr(states), _ptr(w_hard),
+                                  _ptr(ws), _spec_bytes(ws, "ws", 0), _stream(dev))
     _check(st, "viterbi_decode")
     return states, w_hard
 
@@ -275,21 +367,36 @@ def dense_workspace(S, B, L, which, device="cuda"):
     return torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
 
 
+def _dense_shape(theta, codebook, w):
+    """(S, B, L) of a dense call: the codebook is [S], theta [S, S], w [B, L]."""
+    B, L = _chains2(w, "w")
+    _spec(codebook, "codebook", F32, None)
+    if codebook.dim() != 1:
+        raise ValueError(f"codebook must have shape [S], got {tuple(codebook.shape)}")
+    S = int(codebook.numel())
+    _spec(theta, "theta", F32, (S, S))
+    return S, B, L
+
+
 def bcjr_dense_forward(theta, codebook, w, T, w_hat=None, log_z=None, saved=None, ws=None):
     """Dense trellis: soft codeword w_hat [B,L] and log Z [B]; returns (w_hat, log_z, saved)."""
-    _f32(theta, "theta"); _f32(codebook, "codebook"); _f32(w, "w")
-    S = codebook.numel()
-    B, L = w.shape
-    dev = w.device
+    S, B, L = _dense_shape(theta, codebook, w)
+    _spec(w_hat, "w_hat", F32, (B, L))
+    _spec(log_z, "log_z", F32, (B,))
+    need_saved = bcjr_dense_saved_bytes(S, B, L)
+    _spec_bytes(saved, "saved", need_saved)
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, theta, w_hat, log_z, saved, ws)
     w_hat = torch.empty_like(w) if w_hat is None else w_hat
-    log_z = torch.empty(B, dtype=torch.float32, device=dev) if log_z is None else log_z
+    log_z = torch.empty(B, dtype=F32, device=dev) if log_z is None else log_z
     if saved is None:
-        saved = torch.empty(max(bcjr_dense_saved_bytes(S, B, L), 1), dtype=torch.uint8, device=dev)
+        saved = torch.empty(max(need_saved, 1), dtype=torch.uint8, device=dev)
     if ws is None:
         ws = dense_workspace(S, B, L, FWD, dev)
-    st = lib().bcjr_dense_forward(S, _ptr(theta), _ptr(codebook), _ptr(w), B, L, float(T),
-                                  _ptr(w_hat), _ptr(log_z), _ptr(saved), _ptr(ws), ws.numel(),
-                                  _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_dense_forward(S, _ptr(theta), _ptr(codebook), _ptr(w), B, L, float(T),
+                                      _ptr(w_hat), _ptr(log_z), _ptr(saved), _ptr(ws),
+                                      _spec_bytes(ws, "ws", 0), _stream(dev))
     _check(st, "bcjr_dense_forward")
     return w_hat, log_z, saved
 
@@ -298,21 +405,28 @@ def bcjr_dense_backward(theta, codebook, w, T, saved, grad_w_hat, grad_log_z=Non
                         grad_codebook=None, grad_theta=None, ws=None):
     """Dense trellis gradient of sum(g * w_hat) + sum(h * log_z); returns
     (grad_w, grad_codebook, grad_theta)."""
-    _f32(theta, "theta"); _f32(codebook, "codebook"); _f32(w, "w"); _f32(grad_w_hat, "grad_w_hat")
-    if grad_log_z is not None:
-        _f32(grad_log_z, "grad_log_z")
-    S = codebook.numel()
-    B, L = w.shape
-    dev = w.device
+    S, B, L = _dense_shape(theta, codebook, w)
+    if saved is None:
+        raise ValueError("saved (the forward's context) is required")
+    _spec_bytes(saved, "saved", bcjr_dense_saved_bytes(S, B, L))
+    _spec(grad_w_hat, "grad_w_hat", F32, (B, L))
+    _spec(grad_log_z, "grad_log_z", F32, (B,))
+    _spec(grad_w, "grad_w", F32, (B, L))
+    _spec(grad_codebook, "grad_codebook", F32, (S,))
+    _spec(grad_theta, "grad_theta", F32, (S, S))
+    _spec_bytes(ws, "ws", 0)
+    dev = _device(w, codebook, theta, saved, grad_w_hat, grad_log_z, grad_w, grad_codebook,
+                  grad_theta, ws)
     grad_w = torch.empty_like(w) if grad_w is None else grad_w
     grad_codebook = torch.empty_like(codebook) if grad_codebook is None else grad_codebook
     grad_theta = torch.empty_like(theta) if grad_theta is None else grad_theta
     if ws is None:
         ws = dense_workspace(S, B, L, BWD, dev)
-    st = lib().bcjr_dense_backward(S, _ptr(theta), _ptr(codebook), _ptr(w), B, L, float(T),
-                                   _ptr(saved), _ptr(grad_w_hat), _ptr(grad_log_z), _ptr(grad_w),
-                                   _ptr(grad_codebook), _ptr(grad_theta), _ptr(ws), ws.numel(),
-                                   _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_dense_backward(S, _ptr(theta), _ptr(codebook), _ptr(w), B, L, float(T),
+                                       _ptr(saved), _ptr(grad_w_hat), _ptr(grad_log_z),
+                                       _ptr(grad_w), _ptr(grad_codebook), _ptr(grad_theta),
+                                       _ptr(ws), _spec_bytes(ws, "ws", 0), _stream(dev))
     _check(st, "bcjr_dense_backward")
     return grad_w, grad_codebook, grad_theta
 
@@ -327,31 +441,37 @@ def bcjr_code_words(n: int, k: int, L: int) -> int:
 def bcjr_pack_code(states, n, k, code=None):
     """Pack int32 state paths [B,L] into uint32 codes [B, words] (n bits of s_0, then k bits per
     step, most significant first)."""
-    if not (states.dtype == torch.int32 and states.is_cuda and states.is_contiguous()):
-        raise ValueError("states must be a contiguous int32 CUDA tensor")
-    B, L = states.shape
+    B, L = _chains2(states, "states", I32)
+    words = bcjr_code_words(n, k, L)
+    _spec(code, "code", U32, (B, words))
+    dev = _device(states, code)
     if code is None:
-        code = torch.empty((B, max(bcjr_code_words(n, k, L), 1)), dtype=torch.uint32,
-                           device=states.device)
+        code = torch.empty((B, max(words, 1)), dtype=U32, device=dev)
     tr = trellis(n, k)
-    st = lib().bcjr_pack_code(ctypes.byref(tr), _ptr(states), B, L, _ptr(code), _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_pack_code(ctypes.byref(tr), _ptr(states), B, L, _ptr(code), _stream(dev))
     _check(st, "bcjr_pack_code")
     return code
 
 
 def bcjr_unpack_code(code, n, k, L, codebook=None, states=None, w_hard=None):
     """States int32 [B,L] (and w_hard = c(states) if a codebook is given) from uint32 codes."""
-    if not (code.dtype == torch.uint32 and code.is_cuda and code.is_contiguous()):
-        raise ValueError("code must be a contiguous uint32 CUDA tensor")
-    B = code.shape[0]
-    dev = code.device
-    states = torch.empty((B, L), dtype=torch.int32, device=dev) if states is None else states
-    if codebook is not None:
-        _f32(codebook, "codebook")
-        if w_hard is None:
-            w_hard = torch.empty((B, L), dtype=torch.float32, device=dev)
+    B, nw = _chains2(code, "code", U32)
+    words = bcjr_code_words(n, k, L)
+    if nw != words:
+        raise ValueError(f"code has {nw} words per chain; n={n}, k={k}, L={L} need {words}")
+    _spec(codebook, "codebook", F32, (1 << int(n),))
+    _spec(states, "states", I32, (B, L))
+    _spec(w_hard, "w_hard", F32, (B, L))
+    if w_hard is not None and codebook is None:
+        raise ValueError("w_hard needs the codebook")
+    dev = _device(code, codebook, states, w_hard)
+    states = torch.empty((B, L), dtype=I32, device=dev) if states is None else states
+    if codebook is not None and w_hard is None:
+        w_hard = torch.empty((B, L), dtype=F32, device=dev)
     tr = trellis(n, k, codebook)
-    st = lib().bcjr_unpack_code(ctypes.byref(tr), _ptr(code), B, L, _ptr(states), _ptr(w_hard),
-                                _stream())
+    with torch.cuda.device(dev):
+        st = lib().bcjr_unpack_code(ctypes.byref(tr), _ptr(code), B, L, _ptr(states),
+                                    _ptr(w_hard), _stream(dev))
     _check(st, "bcjr_unpack_code")
     return states, w_hard

@@ -30,9 +30,10 @@ FLAGS = [
 ]
 SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kernels.hip", "code_kernels.hip",
            "scan_kernels.hip"]
-# The forward-backward kernels assume finite inputs (NaN in w, the codebook or theta gives
-# unspecified outputs), so their max reductions need no NaN canonicalisation; the Viterbi
-# decoder keeps strict IEEE semantics for its bit-exact contract.
+# The forward-backward kernels' max reductions need no NaN canonicalisation: a NaN or Inf input
+# still reaches the outputs through the exponentials and sums that follow every max (the
+# propagation the C ABI documents is tested); the Viterbi decoder keeps strict IEEE semantics
+# for its bit-exact contract.
 EXTRA_FLAGS = {"sparse_kernels.hip": ["-fno-honor-nans"], "dense_kernels.hip": ["-fno-honor-nans"]}
 
 

@@ -47,6 +47,15 @@ constexpr int geom_spb(int n, int k, int kind) {
 constexpr int geom_block(int n, int k, int kind) {
   return geom_lps(n, k, kind) < 64 ? 64 : geom_lps(n, k, kind);
 }
+// Below this temperature the forward-backward carries its messages in fp64 (their fp32
+// rounding, which grows like 1/T, would put the gradient outside 1e-3). The fp64-message
+// backward needs both of a chain's message buffers (fp64 + fp32 per butterfly, single-buffered)
+// in LDS; shapes where they do not fit (S = 2^16 at k = 2) have no fp64-message kernels and the
+// entry points refuse temperatures below the threshold for them.
+constexpr float kPreciseBelowT = 0.01f;
+constexpr bool geom_precise_fits(int n, int k) {
+  return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;
+}
 // Blocks are persistent: each loops over chain units. Workspace slots cover the largest
 // resident grid on a 256-CU device at 8 waves per SIMD (32 per CU); a launch uses
 // min(slots, resident blocks) of them.
@@ -60,5 +69,6 @@ static_assert(geom_g(16, 2, kBwd) == 4 && geom_lps(16, 2, kBwd) == 1024, "S=6553
 static_assert(geom_g(4, 2, kFwd) == 1 && geom_lps(4, 2, kFwd) == 1, "S=16 geometry");
 static_assert(geom_g(8, 2, kBwd) == 2 && geom_lps(8, 2, kBwd) == 8, "S=256 geometry");
 static_assert(geom_g(8, 2, kFwdS) == 1 && geom_lps(8, 2, kBwdS) == 16, "S=256 segment geometry");
+static_assert(geom_precise_fits(15, 2) && !geom_precise_fits(16, 2), "fp64 messages up to S=2^15");
 
 }  // namespace bcjr

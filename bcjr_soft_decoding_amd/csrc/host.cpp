@@ -85,9 +85,15 @@ bool shape_ok(const bcjr_trellis* tr) {
 }
 
 // Common validation. On success fills *g (for B > 0) and returns BCJR_OK.
+// B * L is bounded by 2^40 (L alone too), which keeps every element offset, workspace size and
+// history size of the sparse kernels exact in 64-bit arithmetic.
+bool chains_ok(int64_t B, int64_t L) {
+  return B >= 0 && L >= 1 && L <= ((int64_t)1 << 40) && (B == 0 || B <= ((int64_t)1 << 40) / L);
+}
+
 bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, int kind, SparseGeom* g) {
   if (tr == nullptr) return BCJR_E_ARG;
-  if (!shape_ok(tr) || B < 0 || L < 1) return BCJR_E_SHAPE;
+  if (!shape_ok(tr) || !chains_ok(B, L)) return BCJR_E_SHAPE;
   if (tr->weights_per_step != 1) return BCJR_E_UNSUPPORTED;
   if (!sparse_geom(tr->state_bits, tr->bits_per_step, B, kind, g)) return BCJR_E_UNSUPPORTED;
   if (B > 0 && tr->codebook == nullptr) return BCJR_E_ARG;
@@ -95,6 +101,12 @@ bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, int kind,
 }
 
 bool temp_ok(float T) { return isfinite(T) && T > 0.0f; }
+
+// Shapes without fp64-message kernels (geom_precise_fits false) keep fp32 messages, whose
+// rounding puts the gradient outside 1e-3 below kPreciseBelowT: refused there.
+bool temp_supported(const bcjr_trellis* tr, float T) {
+  return T >= kPreciseBelowT || geom_precise_fits(tr->state_bits, tr->bits_per_step);
+}
 
 // Workspaces are accessed with 16-byte vector loads and stores.
 bool ws_ok(const void* ws, size_t have, size_t need) {
@@ -141,7 +153,7 @@ bcjr_status scan_setup(const bcjr_trellis* tr, int64_t B, int64_t L, int64_t seg
   const int64_t s_eff = seg < L ? seg : L;
   const int64_t pmain = L / s_eff;
   const int64_t ptot = pmain + (L % s_eff ? 1 : 0);
-  if (B > 0 && ptot > ((int64_t)1 << 58) / (B * M * M * 4)) return BCJR_E_SHAPE;
+  if (B > 0 && ptot > ((int64_t)1 << 56) / M / M / B) return BCJR_E_SHAPE;
   // the segments run with the segment geometry (fp32 messages) or the fp64 one; the plan's
   // history sizes take the larger of the two (sparse_fwd_ws_bytes)
   SparseGeom gm, gt;
@@ -318,12 +330,12 @@ int bcjr_supported(const bcjr_trellis* tr) {
 }
 
 size_t bcjr_saved_bytes(const bcjr_trellis* tr, int64_t B, int64_t L) {
-  if (tr == nullptr || !shape_ok(tr) || B < 0 || L < 1) return 0;
+  if (tr == nullptr || !shape_ok(tr) || !chains_ok(B, L)) return 0;
   return round256(bcjr::saved_bytes(B, L));
 }
 
 size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int which) {
-  if (tr == nullptr || !shape_ok(tr) || B < 0 || L < 1 || tr->weights_per_step != 1) return 0;
+  if (tr == nullptr || !shape_ok(tr) || !chains_ok(B, L) || tr->weights_per_step != 1) return 0;
   if (which < 0 || which > 4) return 0;
   const int kind = which == 3 ? kFwd : which == 4 ? kBwd : which;
   SparseGeom g;
@@ -346,8 +358,10 @@ bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int6
   bcjr_status st = check_common(tr, B, L, kFwd, &g);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
+  if (!temp_supported(tr, T)) return BCJR_E_UNSUPPORTED;
   if (B == 0) return BCJR_OK;
   if (!w || !w_hat || !log_z || !saved) return BCJR_E_ARG;
+  if (((uintptr_t)saved & 15) != 0) return BCJR_E_ARG;
   bool ckpt = false;
   st = pick_layout(ws, ws_bytes, sparse_fwd_ws_bytes(g, L, false), sparse_fwd_ws_bytes(g, L, true),
                    &ckpt);
@@ -364,12 +378,14 @@ bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int
   bcjr_status st = check_common(tr, B, L, kBwd, &g);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
+  if (!temp_supported(tr, T)) return BCJR_E_UNSUPPORTED;
   if (grad_codebook == nullptr) return BCJR_E_ARG;
   if (B == 0) {
     // no chain contributes: the summed codebook gradient is zero
     return from_hip(launch_fill_zero(grad_codebook, (int64_t)1 << tr->state_bits, stream));
   }
   if (!w || !saved || !grad_w_hat || !grad_w) return BCJR_E_ARG;
+  if (((uintptr_t)saved & 15) != 0) return BCJR_E_ARG;
   bool ckpt = false;
   st = pick_layout(ws, ws_bytes, sparse_bwd_ws_bytes(g, L, false), sparse_bwd_ws_bytes(g, L, true),
                    &ckpt);
@@ -440,6 +456,7 @@ bcjr_status bcjr_dense_forward(int32_t S, const float* theta, const float* codeb
   bcjr_status st = dense_check(S, B, L);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
+  if (T < kDenseMinT) return BCJR_E_UNSUPPORTED;
   if (B == 0) return BCJR_OK;
   if (!theta || !codebook || !w || !w_hat || !log_z || !saved) return BCJR_E_ARG;
   if (((uintptr_t)saved & 15) != 0) return BCJR_E_ARG;
@@ -458,6 +475,7 @@ bcjr_status bcjr_dense_backward(int32_t S, const float* theta, const float* code
   bcjr_status st = dense_check(S, B, L);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
+  if (T < kDenseMinT) return BCJR_E_UNSUPPORTED;
   if (!grad_codebook || !grad_theta) return BCJR_E_ARG;
   if (B == 0) {
     // no chain contributes: both summed gradients are zero

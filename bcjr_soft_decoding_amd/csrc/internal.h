@@ -271,6 +271,13 @@ inline void dense_layout(int S, int64_t B, int64_t L, DenseLayout* d) {
   d->bwd = d->gp + round256((size_t)kDenseGemmMaxGrid * S * S * sizeof(float));
 }
 
+// The dense path works in the linear domain: with every step rescaled to its maximum, a state
+// whose relative weight falls below 2^-126 is dropped. At unit-scale theta, c and w this keeps
+// ŵ and the gradients within tolerance down to T = 0.1 (measured on MI355X for S = 32 ... 256:
+// at T = 0.05 ŵ errs by 4e-3 at S = 256, and below 0.03 whole steps underflow to NaN), so the
+// entry points refuse lower temperatures.
+constexpr float kDenseMinT = 0.1f;
+
 // True if dense kernels for S states are compiled in (dense_kernels.hip).
 bool dense_shape_built(int S);
 int launch_dense_forward(int S, const float* theta, const float* codebook, const float* w, int64_t B,

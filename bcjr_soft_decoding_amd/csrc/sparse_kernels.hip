@@ -1951,14 +1951,13 @@ k_reduce_slots(const float* __restrict__ partial, long long slots, long long cou
   out[s] = acc;
 }
 
-// Messages are carried in fp64 below this temperature, for every shape whose backward
-// message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS. The fp64-message
-// kernels use their own lane geometry (kFwdP / kBwdP): fewer states per lane, since every
-// message takes two registers.
-constexpr float kPreciseBelowT = 0.01f;
+// Messages are carried in fp64 below kPreciseBelowT (geom.h), for every shape whose backward
+// message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS; the host layer
+// refuses lower temperatures for the other shapes. The fp64-message kernels use their own lane
+// geometry (kFwdP / kBwdP): fewer states per lane, since every message takes two registers.
 template <int n, int k>
 constexpr bool precise_fits() {
-  return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;
+  return geom_precise_fits(n, k);
 }
 template <class P>
 constexpr int fwd_kind() { return P::kPrecise ? kFwdP : kFwd; }

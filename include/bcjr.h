@@ -30,11 +30,12 @@
  *     nothing is enqueued and no output buffer is touched.
  *   - Calls are asynchronous on the given stream (NULL = the default stream) and never
  *     synchronise. A launch failure is reported as BCJR_E_DEVICE by the call that sees it.
- *   - Inputs are not checked for NaN or Inf: the forward-backward entry points assume finite
- *     w, codebook and theta (NaN gives unspecified outputs); the Viterbi decoder is IEEE-exact.
- *     Chains are independent: a NaN or Inf in one chain's weights leaves every other chain's
- *     w_hat, log_z, grad_w and decoded path unchanged (it reaches the gradients that sum over
- *     chains: the codebook's and theta's).
+ *   - Inputs are not checked for NaN or Inf; non-finite values propagate. A NaN or +-Inf in
+ *     one chain's weights makes that chain's w_hat, log_z and grad_w NaN, and the gradients
+ *     that sum over chains (the codebook's and theta's) NaN; every other chain's w_hat, log_z,
+ *     grad_w and decoded path are bitwise unchanged (chains are independent). A NaN or Inf in
+ *     the codebook or theta makes every output of the call NaN. The Viterbi decoder is
+ *     IEEE-exact.
  *   - Results are bitwise deterministic for a given device, input and argument set.
  *   - The library is thread safe (no shared mutable state); use one stream per thread.
  */
@@ -98,9 +99,15 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
  * w_hat  DEVICE [B,L]  written
  * log_z  DEVICE [B]    written
  * saved  DEVICE, bcjr_saved_bytes() bytes, written; pass it unchanged to bcjr_backward
+ * saved  DEVICE, 16-byte aligned (BCJR_E_ARG otherwise)
  * ws     DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 3) (checkpointed history) or
  *        >= bcjr_workspace_bytes(tr, B, L, 0) (full history); contents are scratch
- * B = 0 is valid and enqueues nothing.
+ * B = 0 is valid and enqueues nothing. B * L may not exceed 2^40 (BCJR_E_SHAPE).
+ * Temperature and precision: below T = 0.01 the messages are carried in fp64 (their fp32
+ * rounding grows like 1/T and would put the gradient outside 1e-3), above in fp32. The fp64
+ * kernels exist for every state size whose backward message buffers fit the 160 KiB of LDS,
+ * i.e. n <= 15 at k = 2; for n = 16 (S = 2^16) bcjr_forward and bcjr_backward return
+ * BCJR_E_UNSUPPORTED when T < 0.01, before enqueueing anything (at T >= 0.01 they run).
  */
 bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                          float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,
@@ -118,9 +125,8 @@ bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int6
  * grad_codebook DEVICE [S] written (overwritten, summed over all B chains, fixed-order sum)
  * ws         DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 4) (checkpointed history) or
  *            >= bcjr_workspace_bytes(tr, B, L, 1) (full history)
- * Precision: messages are fp64 below T = 0.01 and fp32 above, except at S = 2^16, where they are
- * fp32 at every T (fp64 would not fit LDS); there, below T = 0.01, grad_w can lose accuracy
- * beyond 1e-3 on inputs whose paths nearly tie (w_hat, log_z and grad_codebook do not).
+ * Errors as bcjr_forward, including BCJR_E_UNSUPPORTED for S = 2^16 below T = 0.01 (there the
+ * fp32-message gradient erred by up to 0.51 on an input with nearly tied paths).
  */
 bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                           const void* saved, const float* grad_w_hat, const float* grad_log_z,
@@ -243,9 +249,13 @@ bcjr_status bcjr_unpack_code(const bcjr_trellis* tr, const uint32_t* code, int64
  * "Key technical innovations": O(L*S^2) forward-backward with exact gradients through the
  * trellis parameters), run as rescaled linear-domain matrix products on the matrix cores.
  * Messages are fp32 in the linear domain, rescaled every step; a state whose relative weight
- * falls below the fp32 range (2^-126 of the step's best) is dropped. Intended for moderate T
- * (validated for T in [0.1, 5] with theta, c and w of unit scale); use the bitshift entry points
- * for the near-hard regime.
+ * falls below the fp32 range (2^-126 of the step's best) is dropped. That limits the path to
+ * moderate T: at theta, c and w of unit scale it meets the tolerances from T = 0.1 up (tested
+ * to T = 5), while at T = 0.05 w_hat errs by 4e-3 and below T = 0.03 whole steps underflow.
+ * Both dense entry points therefore return BCJR_E_UNSUPPORTED for T < 0.1. Inputs of scale
+ * lam behave like unit-scale ones at T / lam^2 ((w, c, theta, T) -> (lam w, lam c, lam^2 theta,
+ * lam^2 T) leaves the posteriors unchanged), so T >= 0.1 lam^2 is the range to use. The
+ * bitshift entry points cover the near-hard regime.
  * Supported S: 32, 64, 128, 256 (bcjr_dense_supported). B >= 0, L >= 1.
  */
 

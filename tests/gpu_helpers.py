@@ -59,3 +59,23 @@ def run_fwd_bwd(n, k, c, w, T, g=None, h=None):
         out.update(grad_w=gw, grad_codebook=gc)
     torch.cuda.synchronize()
     return {key: v.cpu().numpy() for key, v in out.items()}
+
+
+def assert_refused(n, k, c, w, T, g):
+    """A (shape, T) without kernels that meet the tolerances: forward and backward raise
+    BCJR_E_UNSUPPORTED before launching anything, and leave their outputs untouched."""
+    import pytest
+
+    cd, wd = dev(c), dev(w)
+    B, L = w.shape
+    w_hat = torch.full_like(wd, 7.0)
+    with pytest.raises(bcjr.BcjrError) as e:
+        bcjr.bcjr_forward(cd, wd, n, k, T, w_hat=w_hat)
+    assert e.value.status == bcjr.BCJR_E_UNSUPPORTED
+    saved = torch.zeros(max(bcjr.bcjr_saved_bytes(n, k, B, L), 1), dtype=torch.uint8, device="cuda")
+    gc = torch.full_like(cd, 7.0)
+    with pytest.raises(bcjr.BcjrError) as e:
+        bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), grad_codebook=gc)
+    assert e.value.status == bcjr.BCJR_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(w_hat == 7.0) and torch.all(gc == 7.0)

@@ -95,8 +95,30 @@ def test_forward_rejects_bad_arguments_without_device(lib):
     need = bcjr.bcjr_workspace_bytes(8, 2, 4, 8, bcjr.FWD_CKPT)  # the smaller, checkpointed layout
     assert _fwd(lib, wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
     assert _fwd(lib, ws=0x6008) == bcjr.BCJR_E_WORKSPACE  # 16-byte alignment
+    assert _fwd(lib, sv=0x5008) == bcjr.BCJR_E_ARG  # the context holds doubles: 16-byte aligned
     # B = 0 is valid and enqueues nothing (null outputs allowed)
     assert _fwd(lib, B=0, w=0, wh=0, lz=0, sv=0, ws=0, wsb=0) == bcjr.BCJR_OK
+    # B * L beyond 2^40 (64-bit offsets and workspace sizes stay exact below it)
+    assert _fwd(lib, B=1 << 21, L=1 << 20) == bcjr.BCJR_E_SHAPE
+    assert _fwd(lib, B=1, L=(1 << 40) + 1) == bcjr.BCJR_E_SHAPE
+
+
+def test_temperatures_below_the_fp64_threshold_need_fp64_kernels(lib):
+    """Below T = 0.01 the messages must be fp64; the 2^16-state trellis has no such kernels
+    (its message buffers would not fit LDS) and is refused there, before any device call."""
+    for T in (0.0099, 0.005, 1e-4):
+        assert _fwd(lib, n=16, T=T) == bcjr.BCJR_E_UNSUPPORTED
+        assert _fwd(lib, n=16, T=T, B=0, w=0, wh=0, lz=0, sv=0, ws=0, wsb=0) == bcjr.BCJR_E_UNSUPPORTED
+    P = ctypes.c_void_p
+    tr = bcjr.Trellis(16, 2, 1, 0x1000)
+    st = lib.bcjr_backward(ctypes.byref(tr), P(0x2000), 4, 8, 0.005, P(0x3000), P(0x4000), None,
+                           P(0x5000), P(0x6000), P(0x7000), 1 << 40, None)
+    assert st == bcjr.BCJR_E_UNSUPPORTED
+    # at the threshold, and for every smaller trellis, validation passes (the call then needs a
+    # device: not made here, so only the status of a refused workspace is observed)
+    assert _fwd(lib, n=16, T=0.01, wsb=0) == bcjr.BCJR_E_WORKSPACE
+    for n in range(4, 16):
+        assert _fwd(lib, n=n, T=0.001, wsb=0) == bcjr.BCJR_E_WORKSPACE
 
 
 def test_backward_and_viterbi_reject_bad_arguments_without_device(lib):
@@ -181,6 +203,13 @@ def test_dense_rejects_bad_arguments_without_device(lib):
     assert bwd(gc=P(0)) == bcjr.BCJR_E_ARG
     assert bwd(g=P(0)) == bcjr.BCJR_E_ARG
     assert bwd(S=100) == bcjr.BCJR_E_UNSUPPORTED
+    # the linear-domain dense path is refused below T = 0.1 (its states underflow there)
+    for T in (0.0999, 0.05, 0.01):
+        assert fwd(T=T) == bcjr.BCJR_E_UNSUPPORTED
+        assert bwd(T=T) == bcjr.BCJR_E_UNSUPPORTED
+        assert fwd(T=T, B=0, th=P(0), w=P(0), wh=P(0), lz=P(0), sv=P(0), ws=P(0), wsb=0) == \
+            bcjr.BCJR_E_UNSUPPORTED
+    assert fwd(T=0.1, wsb=0) == bcjr.BCJR_E_WORKSPACE  # accepted from 0.1 on
     need = bcjr.bcjr_dense_workspace_bytes(64, 4, 8, 1)
     assert bwd(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
 

@@ -1,0 +1,117 @@
+"""The Python binding rejects every mis-sized tensor before anything reaches the C ABI (which
+sees only raw pointers and could not tell a short buffer from a long one). Runs without a GPU:
+shapes and dtypes are checked before the tensors' device, so CPU tensors exercise every check,
+and a call whose shapes are all right stops at the device check, still before any launch."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from bcjr_soft_decoding_amd import bcjr
+
+N, K, B, L = 8, 2, 3, 5
+S = 1 << N
+
+
+def f32(*shape):
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    bcjr.lib()  # the size queries below call the library (host code only)
+
+
+def raises(fn, *words):
+    with pytest.raises((ValueError, TypeError)) as e:
+        fn()
+    msg = str(e.value)
+    for wd in words:
+        assert wd in msg, (wd, msg)
+    return msg
+
+
+def test_forward_checks_every_tensor():
+    c, w = f32(S), f32(B, L)
+    raises(lambda: bcjr.bcjr_forward(f32(S - 1), w, N, K, 0.5), "codebook", "shape")
+    raises(lambda: bcjr.bcjr_forward(f32(S, 1), w, N, K, 0.5), "codebook", "shape")
+    raises(lambda: bcjr.bcjr_forward(c, f32(B * L), N, K, 0.5), "w", "[B, L]")
+    raises(lambda: bcjr.bcjr_forward(c, w.double(), N, K, 0.5), "w", "float32")
+    raises(lambda: bcjr.bcjr_forward(c, f32(L, B).t(), N, K, 0.5), "contiguous")
+    raises(lambda: bcjr.bcjr_forward(c, w, N, K, 0.5, w_hat=f32(B, L - 1)), "w_hat")
+    raises(lambda: bcjr.bcjr_forward(c, w, N, K, 0.5, log_z=f32(B + 1)), "log_z")
+    need = bcjr.bcjr_saved_bytes(N, K, B, L)
+    assert need > 0
+    raises(lambda: bcjr.bcjr_forward(c, w, N, K, 0.5, saved=torch.zeros(need - 1, dtype=torch.uint8)),
+           "saved", "bytes")
+    # all shapes right: stops at the device check (no launch, no allocation)
+    raises(lambda: bcjr.bcjr_forward(c, w, N, K, 0.5), "CUDA")
+
+
+def test_backward_checks_every_tensor():
+    c, w, g = f32(S), f32(B, L), f32(B, L)
+    sv = torch.zeros(bcjr.bcjr_saved_bytes(N, K, B, L), dtype=torch.uint8)
+    raises(lambda: bcjr.bcjr_backward(f32(S // 2), w, N, K, 0.5, sv, g), "codebook")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, sv[:-8], g), "saved")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, None, g), "saved")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, sv, f32(B, L + 1)), "grad_w_hat")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, sv, g, f32(B - 1)), "grad_log_z")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, sv, g, grad_w=f32(B)), "grad_w")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, sv, g, grad_codebook=f32(S - 1)),
+           "grad_codebook")
+    raises(lambda: bcjr.bcjr_backward(c, w, N, K, 0.5, sv, g), "CUDA")
+
+
+def test_viterbi_and_code_check_every_tensor():
+    c, w = f32(S), f32(B, L)
+    raises(lambda: bcjr.viterbi_decode(f32(3), w, N, K), "codebook")
+    raises(lambda: bcjr.viterbi_decode(c, w, N, K, states=torch.zeros((B, L), dtype=torch.int64)),
+           "states", "int32")
+    raises(lambda: bcjr.viterbi_decode(c, w, N, K, states=torch.zeros((B, L + 1), dtype=torch.int32)),
+           "states", "shape")
+    raises(lambda: bcjr.viterbi_decode(c, w, N, K, w_hard=f32(B)), "w_hard")
+    st = torch.zeros((B, L), dtype=torch.int32)
+    words = bcjr.bcjr_code_words(N, K, L)
+    raises(lambda: bcjr.bcjr_pack_code(st, N, K, code=torch.zeros((B, words + 1), dtype=torch.uint32)),
+           "code")
+    raises(lambda: bcjr.bcjr_unpack_code(torch.zeros((B, words + 1), dtype=torch.uint32), N, K, L),
+           "words")
+    code = torch.zeros((B, words), dtype=torch.uint32)
+    raises(lambda: bcjr.bcjr_unpack_code(code, N, K, L, codebook=f32(S - 1)), "codebook")
+    raises(lambda: bcjr.bcjr_unpack_code(code, N, K, L, w_hard=f32(B, L)), "codebook")
+    raises(lambda: bcjr.bcjr_unpack_code(code, N, K, L), "CUDA")
+
+
+def test_segmented_entry_points_check_every_tensor():
+    c, w = f32(S), f32(B, L)
+    raises(lambda: bcjr.bcjr_forward_scan(f32(S + 1), w, N, K, 0.5), "codebook")
+    raises(lambda: bcjr.bcjr_forward_scan(c, w, N, K, 0.5, w_hat=f32(B)), "w_hat")
+    raises(lambda: bcjr.bcjr_backward_scan(c, w, N, K, 0.5, f32(B, L - 1), w), "w_hat")
+    raises(lambda: bcjr.bcjr_backward_scan(c, w, N, K, 0.5, w, w, grad_codebook=f32(2)),
+           "grad_codebook")
+    raises(lambda: bcjr.bcjr_backward_scan(c, w, N, K, 0.5, w, w), "CUDA")
+
+
+def test_dense_entry_points_check_every_tensor():
+    Sd = 32
+    th, c, w = f32(Sd, Sd), f32(Sd), f32(B, L)
+    raises(lambda: bcjr.bcjr_dense_forward(f32(Sd, Sd - 1), c, w, 0.5), "theta")
+    raises(lambda: bcjr.bcjr_dense_forward(th, f32(Sd, 1), w, 0.5), "codebook")
+    raises(lambda: bcjr.bcjr_dense_forward(th, c, w, 0.5, log_z=f32(1)), "log_z")
+    need = bcjr.bcjr_dense_saved_bytes(Sd, B, L)
+    sv = torch.zeros(need, dtype=torch.uint8)
+    raises(lambda: bcjr.bcjr_dense_forward(th, c, w, 0.5, saved=sv[: need // 2]), "saved")
+    raises(lambda: bcjr.bcjr_dense_backward(th, c, w, 0.5, sv, f32(B, L), grad_theta=f32(Sd)),
+           "grad_theta")
+    raises(lambda: bcjr.bcjr_dense_backward(th, c, w, 0.5, sv, f32(B, L), grad_codebook=f32(Sd + 1)),
+           "grad_codebook")
+    raises(lambda: bcjr.bcjr_dense_backward(th, c, w, 0.5, sv[:16], f32(B, L)), "saved")
+    raises(lambda: bcjr.bcjr_dense_backward(th, c, w, 0.5, sv, f32(B, L)), "CUDA")
+
+
+def test_library_path_has_no_override():
+    """The product binding loads the in-tree library only; no environment variable redirects it."""
+    import inspect
+
+    assert bcjr.LIB_PATH.endswith("bcjr_soft_decoding_amd/_lib/libbcjr.so")
+    assert "environ" not in inspect.getsource(bcjr)

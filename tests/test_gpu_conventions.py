@@ -39,14 +39,17 @@ def _sparse(n, c, w, g, h, T, ckpt=False):
     wf = bcjr.workspace(n, k, B, L, bcjr.FWD_CKPT if ckpt else bcjr.FWD)
     wb = bcjr.workspace(n, k, B, L, bcjr.BWD_CKPT if ckpt else bcjr.BWD)
     w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, k, T, ws=wf)
-    gw, _ = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), dev(h), ws=wb)
+    gw, gc = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), dev(h), ws=wb)
     states, w_hard = bcjr.viterbi_decode(cd, wd, n, k)
     torch.cuda.synchronize()
-    return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard}
+    return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard,
+            "grad_codebook": gc}
 
 
 def _check_isolated(clean, poisoned, j, what):
     for key, a in clean.items():
+        if key == "grad_codebook":  # a sum over chains
+            continue
         a = a.cpu().numpy()
         b = poisoned[key].cpu().numpy()
         others = np.arange(a.shape[0]) != j
@@ -78,6 +81,66 @@ def test_nan_stays_in_its_chain(n, B, L, T, ckpt):
     poisoned = _sparse(n, c, w2, g, h, T, ckpt)
     _check_isolated(clean, poisoned, j, f"n={n}")
     assert np.all(np.isnan(poisoned["w_hat"][j].cpu().numpy())), "NaN did not reach w_hat"
+
+
+# NaN or Inf in the inputs propagates (nothing is checked or reported): a non-finite weight
+# makes its chain's w_hat, log_z and grad_w NaN and, through the sum over chains, the codebook
+# gradient; a non-finite codebook entry or theta entry reaches every chain.
+@pytest.mark.parametrize("n,B,L,T", [(8, 20, 30, 0.3), (12, 6, 20, 0.1), (10, 6, 20, 0.005),
+                                     (16, 3, 8, 0.3)])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), -float("inf")])
+def test_non_finite_weight_propagates(n, B, L, T, bad):
+    log_case(f"non-finite weight {bad} n={n} B={B} L={L} T={T}")
+    c, w, g, h = _inputs(n, B, L, 300 + n)
+    j = B // 2
+    w[j, L // 3] = bad
+    out = _sparse(n, c, w, g, h, T)
+    for key in ("w_hat", "grad_w"):
+        assert np.all(np.isnan(out[key][j].cpu().numpy())), f"{key} of the chain is not all NaN"
+    assert np.isnan(out["log_z"][j].item())
+    assert np.all(np.isnan(out["grad_codebook"].cpu().numpy())), "grad_codebook is not all NaN"
+
+
+@pytest.mark.parametrize("n", [8, 16])
+def test_non_finite_codebook_entry_reaches_every_chain(n):
+    log_case(f"NaN codebook entry n={n}")
+    B, L, T = 4, 12, 0.3
+    c, w, g, h = _inputs(n, B, L, 400 + n)
+    c[(1 << n) // 3] = np.nan
+    out = _sparse(n, c, w, g, h, T)
+    for key in ("w_hat", "log_z", "grad_w", "grad_codebook"):
+        assert np.all(np.isnan(out[key].cpu().numpy())), f"{key} is not all NaN"
+
+
+def test_non_finite_dense_inputs_propagate():
+    S, B, L, T = 64, 6, 16, 0.3
+    rng = np.random.default_rng(19)
+    theta = rng.standard_normal((S, S)).astype(np.float32)
+    c = rng.standard_normal(S).astype(np.float32)
+    w = rng.standard_normal((B, L)).astype(np.float32)
+    g = rng.standard_normal((B, L)).astype(np.float32)
+
+    def run(th, ww):
+        wh, lz, sv = bcjr.bcjr_dense_forward(dev(th), dev(c), dev(ww), T)
+        gw, gc, gt = bcjr.bcjr_dense_backward(dev(th), dev(c), dev(ww), T, sv, dev(g))
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in
+                dict(w_hat=wh, log_z=lz, grad_w=gw, grad_codebook=gc, grad_theta=gt).items()}
+
+    log_case("dense: NaN weight")
+    w2 = w.copy()
+    w2[2, 7] = np.nan
+    out = run(theta, w2)
+    for key in ("w_hat", "grad_w"):
+        assert np.all(np.isnan(out[key][2])), key
+    assert np.isnan(out["log_z"][2])
+    assert np.all(np.isnan(out["grad_codebook"])) and np.all(np.isnan(out["grad_theta"]))
+    log_case("dense: NaN theta entry")
+    th2 = theta.copy()
+    th2[5, 9] = np.nan
+    out = run(th2, w)
+    for key, v in out.items():
+        assert np.all(np.isnan(v)), key
 
 
 def test_nan_stays_in_its_chain_segmented_and_dense():
@@ -157,10 +220,11 @@ def _sparse_on_stream(n, c, w, g, h, T):
     B, L = w.shape
     cd, wd = dev(c), dev(w)
     w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, k, T)
-    gw, _ = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), dev(h))
+    gw, gc = bcjr.bcjr_backward(cd, wd, n, k, T, saved, dev(g), dev(h))
     states, w_hard = bcjr.viterbi_decode(cd, wd, n, k)
     torch.cuda.current_stream().synchronize()
-    return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard}
+    return {"w_hat": w_hat, "log_z": log_z, "grad_w": gw, "states": states, "w_hard": w_hard,
+            "grad_codebook": gc}
 
 
 @pytest.mark.parametrize("n,T,ckpt", [(8, 0.5, False), (8, 0.5, True), (15, 0.005, False),

@@ -164,3 +164,34 @@ def test_dense_deterministic():
     b = run_dense(theta, c, w, 0.4, g, h)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+@pytest.mark.parametrize("T", [0.099, 0.05, 0.02])
+def test_dense_below_01_refused(T):
+    """The linear-domain dense path drops states whose weight falls below 2^-126 of a step's
+    best; at unit-scale inputs that breaks its tolerances below T = 0.1 (ŵ off by 4e-3 at
+    T = 0.05, whole steps underflowing to NaN below 0.03 on workload-5 shapes). Those
+    temperatures are refused with BCJR_E_UNSUPPORTED, nothing is enqueued and the outputs keep
+    their contents."""
+    S, B, L = 64, 3, 20
+    theta, c, w, g, h = _case(S, B, L, 7600)
+    log_case(f"dense refused T={T}")
+    wh = torch.full((B, L), 7.0, device="cuda")
+    with pytest.raises(bcjr.BcjrError) as e:
+        bcjr.bcjr_dense_forward(dev(theta), dev(c), dev(w), T, w_hat=wh)
+    assert e.value.status == bcjr.BCJR_E_UNSUPPORTED
+    saved = torch.zeros(bcjr.bcjr_dense_saved_bytes(S, B, L), dtype=torch.uint8, device="cuda")
+    gt = torch.full((S, S), 7.0, device="cuda")
+    with pytest.raises(bcjr.BcjrError) as e:
+        bcjr.bcjr_dense_backward(dev(theta), dev(c), dev(w), T, saved, dev(g), grad_theta=gt)
+    assert e.value.status == bcjr.BCJR_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(wh == 7.0) and torch.all(gt == 7.0)
+
+
+def test_dense_workload5_at_the_threshold():
+    """T = 0.1, the lowest temperature the dense path accepts, on workload-5 shapes (S = 256,
+    L = 1024, first 6 chains) against the oracle."""
+    theta, c = synth.theta(5), synth.codebook(5)
+    w, g, h = synth.weights(5)[:6], synth.upstream_grad(5)[:6], synth.logz_grad(5)[:6]
+    compare_dense(theta, c, w, 0.1, g, h, "wl5-threshold")

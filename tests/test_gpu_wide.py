@@ -8,7 +8,8 @@ import torch
 
 import oracle
 from bcjr_soft_decoding_amd import bcjr, synth
-from tests.gpu_helpers import RTOL_FWD, RTOL_GRAD, assert_normwise, assert_rel, dev, log_case
+from tests.gpu_helpers import (RTOL_FWD, RTOL_GRAD, assert_normwise, assert_refused, assert_rel, dev,
+                               log_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +86,36 @@ def test_wide_bitwise_deterministic(n, B, L, T):
         for a, b in zip(outs[0], other):
             assert np.all(np.isfinite(b))
             np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [0.0099, 0.004, 0.002])
+def test_2_16_states_below_001_refused(T):
+    """The 2^16-state trellis has no fp64-message kernels (their two message buffers would not
+    fit LDS), and fp32 messages put the gradient outside 1e-3 on near-tied inputs below T = 0.01
+    (0.51 at T = 0.002 on one input): forward and backward refuse those temperatures with
+    BCJR_E_UNSUPPORTED, enqueue nothing and leave their outputs untouched."""
+    n, B, L = 16, 5, 24
+    log_case(f"n=16 refused T={T}")
+    c = synth.normal(7500, (1 << n,))
+    w = synth.normal(7501, (B, L))
+    g = synth.normal(7502, (B, L))
+    assert_refused(n, 2, c, w, T, g)
+
+
+def test_2_16_states_at_the_threshold_match_oracle():
+    """T = 0.01 exactly, the lowest temperature the 2^16-state kernels accept, against the oracle
+    on the input that erred by 0.51 at T = 0.002 with fp32 messages."""
+    n, B, L, T = 16, 5, 24, 0.01
+    c = synth.normal(7500, (1 << n,))
+    w = synth.normal(7501, (B, L))
+    g = synth.normal(7502, (B, L))
+    h = synth.normal(7503, (B,))
+    ref = oracle.sparse_forward(n, 2, c, w, T)
+    rb = oracle.sparse_backward(n, 2, c, w, T, g, h)
+    for hist in ("full", "ckpt"):
+        log_case(f"n=16 T=0.01 history={hist}")
+        got = _run(n, c, w, g, h, T, hist == "ckpt")
+        assert_normwise(got["w_hat"], ref["w_hat"], RTOL_FWD, f"{hist} w_hat")
+        assert_rel(got["log_z"], ref["log_z"], RTOL_FWD, f"{hist} log_z")
+        assert_normwise(got["grad_w"], rb["grad_w"], RTOL_GRAD, f"{hist} grad_w")
+        assert_normwise(got["grad_codebook"], rb["grad_codebook"], RTOL_GRAD, f"{hist} grad_c")
