@@ -44,7 +44,8 @@ inline size_t saved_bytes(int64_t B, int64_t L) {
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout of the sparse kernels: one slot per persistent block. A forward slot holds
-// the lam history [H][BLOCK][K*G] with 8-byte entries and the shift prefix [L][SPB] (double);
+// the lam history, H entries of BLOCK * K*G values with room for 8 bytes each (each entry in
+// 16-byte chunks interleaved across the block's lanes), and the shift prefix [L][SPB] (double);
 // a backward slot adds the Phi history [H][BLOCK][K*G] (fp32); the backward workspace ends
 // with the codebook-gradient partials [slots][S] (fp32). Sizes do not depend on T.
 // Full history: H = L entries, one per step. Checkpointed history: every C-th step is kept
