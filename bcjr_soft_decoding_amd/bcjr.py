@@ -23,8 +23,10 @@ EXPORTED = (
     "bcjr_dense_workspace_bytes", "bcjr_dense_forward", "bcjr_dense_backward",
     "bcjr_code_words", "bcjr_pack_code", "bcjr_unpack_code", "bcjr_status_string",
     "bcjr_scan_segment_length", "bcjr_scan_workspace_bytes", "bcjr_forward_scan",
-    "bcjr_scan_backward_workspace_bytes", "bcjr_backward_scan",
+    "bcjr_scan_backward_workspace_bytes", "bcjr_backward_scan", "bcjr_forward_noalloc",
 )
+# Size of the fixed device array bcjr_forward_noalloc takes its workspace from.
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class BcjrError(RuntimeError):
@@ -64,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.bcjr_workspace_bytes.restype = SZ
     L.bcjr_forward.argtypes = [TP, P, I64, I64, F, P, P, P, P, SZ, P]
     L.bcjr_forward.restype = ctypes.c_int
+    L.bcjr_forward_noalloc.argtypes = [TP, P, I64, I64, F, P, P, P, P]
+    L.bcjr_forward_noalloc.restype = ctypes.c_int
     L.bcjr_backward.argtypes = [TP, P, I64, I64, F, P, P, P, P, P, P, SZ, P]
     L.bcjr_backward.restype = ctypes.c_int
     L.viterbi_decode.argtypes = [TP, P, I64, I64, P, P, P, SZ, P]
@@ -229,6 +233,27 @@ def bcjr_forward(codebook, w, n, k, T, w_hat=None, log_z=None, saved=None, ws=No
                                 _ptr(log_z), _ptr(saved), _ptr(ws), _spec_bytes(ws, "ws", 0),
                                 _stream(dev))
     _check(st, "bcjr_forward")
+    return w_hat, log_z, saved
+
+
+def bcjr_forward_noalloc(codebook, w, n, k, T, w_hat, log_z, saved):
+    """bcjr_forward with the library's fixed scratch array as workspace: the C entry point makes
+    no device allocation, so every output (w_hat [B,L], log_z [B], saved) is the caller's.
+    Returns (w_hat, log_z, saved)."""
+    B, L = _chains2(w, "w")
+    _spec(codebook, "codebook", F32, (1 << int(n),))
+    for t, name in ((w_hat, "w_hat"), (log_z, "log_z"), (saved, "saved")):
+        if t is None:
+            raise ValueError(f"{name}: bcjr_forward_noalloc writes into caller-owned outputs")
+    _spec(w_hat, "w_hat", F32, (B, L))
+    _spec(log_z, "log_z", F32, (B,))
+    _spec_bytes(saved, "saved", bcjr_saved_bytes(n, k, B, L))
+    dev = _device(w, codebook, w_hat, log_z, saved)
+    tr = trellis(n, k, codebook)
+    with torch.cuda.device(dev):
+        st = lib().bcjr_forward_noalloc(ctypes.byref(tr), _ptr(w), B, L, float(T), _ptr(w_hat),
+                                        _ptr(log_z), _ptr(saved), _stream(dev))
+    _check(st, "bcjr_forward_noalloc")
     return w_hat, log_z, saved
 
 

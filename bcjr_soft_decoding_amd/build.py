@@ -29,7 +29,7 @@ FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kernels.hip", "code_kernels.hip",
-           "scan_kernels.hip"]
+           "scan_kernels.hip", "noalloc.hip"]
 # The forward-backward kernels' max reductions need no NaN canonicalisation: a NaN or Inf input
 # still reaches the outputs through the exponentials and sums that follow every max (the
 # propagation the C ABI documents is tested); the Viterbi decoder keeps strict IEEE semantics

@@ -24,7 +24,7 @@
  *   - Pointers marked DEVICE are device (HBM) pointers; arrays are row-major, contiguous,
  *     fp32 unless stated. "B, L" are the number of chains and the weights per chain.
  *   - The caller owns every buffer. The library allocates no device memory and keeps no
- *     mutable global state. Workspaces (ws) must be 16-byte aligned (BCJR_E_WORKSPACE
+ *     mutable global state, except the fixed scratch array of bcjr_forward_noalloc (below). Workspaces (ws) must be 16-byte aligned (BCJR_E_WORKSPACE
  *     otherwise); their contents on entry are irrelevant and on return unspecified.
  *   - All arguments are validated on the host before anything is enqueued. On any error
  *     nothing is enqueued and no output buffer is touched.
@@ -112,6 +112,30 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
 bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                          float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,
                          bcjr_stream_t stream);
+
+/* ---- Forward that allocates nothing -------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. bcjr_forward (same kernels, same validation, bitwise
+ * the same outputs) with its workspace taken from a fixed device array of the library,
+ * BCJR_NOALLOC_SCRATCH_BYTES long, which the runtime places on every device the library runs on
+ * when it loads the library's code and keeps until the process ends. The call makes no
+ * allocation, free or allocating library call.
+ *   - Shapes whose checkpointed history, bcjr_workspace_bytes(tr, B, L, 3), exceeds
+ *     BCJR_NOALLOC_SCRATCH_BYTES are refused with BCJR_E_WORKSPACE before any device call (at
+ *     S = 4096, L = 256 that admits up to about 1000 chains; the full history is used where it
+ *     fits, else the checkpointed one).
+ *   - The first call on a device (any arguments, B = 0 included) looks up the array's device
+ *     address with that device current (BCJR_E_DEVICE if that fails); make it before any graph
+ *     capture. The stream must belong to the current device, as for every call.
+ *   - Every call on a device shares that device's array, and the array keeps the last call's
+ *     contents (nothing in it needs to start at zero). Calls whose execution overlaps on one
+ *     device (other streams, other threads) race on it: serialise them.
+ * Other arguments and errors as bcjr_forward.
+ */
+#define BCJR_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+bcjr_status bcjr_forward_noalloc(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L,
+                                 float T, float* w_hat, float* log_z, void* saved,
+                                 bcjr_stream_t stream);
 
 /*
  * Backward: exact reverse-mode gradient of  F = sum_{b,t} g[b,t] w_hat[b,t] + sum_b h[b] log_z[b]

@@ -342,3 +342,18 @@ def test_scan_backward_rejects_bad_arguments_without_device(lib):
     assert bscan(wsb=need - 1) == bcjr.BCJR_E_WORKSPACE
     assert bscan(ws=0x6008) == bcjr.BCJR_E_WORKSPACE
     assert bcjr.bcjr_scan_backward_workspace_bytes(8, 2, 0, 64, 16) == 0
+
+
+def test_noalloc_forward_refuses_oversized_shapes_without_device(lib):
+    # the checkpointed history of 2^20 chains of S = 4096 exceeds the fixed array; the refusal
+    # comes before any device call (there is no device here)
+    tr = bcjr.trellis(12, 2, None)
+    P = ctypes.c_void_p
+    B, L = 1 << 20, 256
+    assert bcjr.bcjr_workspace_bytes(12, 2, B, L, 3) > bcjr.NOALLOC_SCRATCH_BYTES
+    st = lib.bcjr_forward_noalloc(ctypes.byref(tr), P(0x2000), B, L, 0.1, P(0x3000), P(0x4000),
+                                  P(0x5000), None)
+    assert st == bcjr.BCJR_E_WORKSPACE
+    header = open(os.path.join(ROOT, "include", "bcjr.h")).read()
+    assert re.search(r"#define BCJR_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", header)
+    assert bcjr.NOALLOC_SCRATCH_BYTES == 256 << 20
