@@ -1108,7 +1108,6 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       }
 }
 
-// out[s] = sum over slots of the partials, in slot order (deterministic); with no slots, 0.
 // ---------------------------------------------------------------------------------------------
 // ---------------------------------------------------------------------------------------------
 // Backward for chains of 1024 lanes. Each message array of a chain (lam / rho and Phi / Psi)
@@ -1620,6 +1619,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   }
 }
 
+// out[s] = sum over slots of the partials, in slot order (deterministic); with no slots, 0.
 __global__ void __launch_bounds__(256)
 k_reduce_slots(const float* __restrict__ partial, long long slots, long long count,
                float* __restrict__ out) {

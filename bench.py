@@ -78,7 +78,8 @@ TRAFFIC_PROFILES = {
     "fwd": os.path.join(ROOT, "profiles", "k_sparse_fwd_llama32-1b-mlp-up-s4096_pmc.md"),
     "bwd": os.path.join(ROOT, "profiles", "k_sparse_bwd_llama32-1b-mlp-up-s4096_pmc.md"),
 }
-KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_decoding_amd/csrc/geom.h",
+KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_decoding_amd/csrc/sparse_device.h",
+                  "bcjr_soft_decoding_amd/csrc/geom.h",
                   "bcjr_soft_decoding_amd/csrc/internal.h", "bcjr_soft_decoding_amd/build.py"]
 
 
