@@ -37,10 +37,22 @@ SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kerne
 EXTRA_FLAGS = {"sparse_kernels.hip": ["-fno-honor-nans"], "dense_kernels.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+# The CPU sanitizer run (tests/run_sanitizers.py) builds a second library whose host code (the
+# validation, size arithmetic and launch set-up) carries AddressSanitizer and
+# UndefinedBehaviorSanitizer; every option applies to the host pass only (the device code is
+# the same as in the ordinary build).
+SAN_LIB = os.path.join(OUT_DIR, "libbcjr_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    bdir = os.path.join(BUILD_DIR, "san") if sanitize else BUILD_DIR
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *(SAN_FLAGS if sanitize else []), *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -51,18 +63,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
+def build(jobs: int = 8, sanitize: bool = False) -> str:
+    """Compile every source for gfx950 and link _lib/libbcjr.so (with sanitize: the
+    host-sanitized _lib/libbcjr_san.so, for the CPU sanitizer run only)."""
     os.makedirs(OUT_DIR, exist_ok=True)
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(os.path.join(BUILD_DIR, "san") if sanitize else BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_FLAGS if sanitize else []), "-o",
+           tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -79,8 +79,7 @@ TRAFFIC_PROFILES = {
     "bwd": os.path.join(ROOT, "profiles", "k_sparse_bwd_llama32-1b-mlp-up-s4096_pmc.md"),
 }
 KERNEL_SOURCES = ["bcjr_soft_decoding_amd/csrc/sparse_kernels.hip", "bcjr_soft_decoding_amd/csrc/sparse_device.h",
-                  "bcjr_soft_decoding_amd/csrc/geom.h",
-                  "bcjr_soft_decoding_amd/csrc/internal.h", "bcjr_soft_decoding_amd/build.py"]
+                  "bcjr_soft_decoding_amd/csrc/geom.h", "bcjr_soft_decoding_amd/csrc/internal.h"]
 
 
 def kernel_names(n: int, k: int):
@@ -102,11 +101,17 @@ def median_ms(pairs):
 
 
 def kernel_source_hash() -> str:
+    """sha256 of the profiled kernels' sources and of the compiler options they are built with
+    (include paths, which name the checkout's location, left out)."""
     import hashlib
+    from bcjr_soft_decoding_amd import build
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    opts = [build.ARCH, [f for f in build.FLAGS if not f.startswith("-I")],
+            build.EXTRA_FLAGS.get("sparse_kernels.hip", [])]
+    h.update(repr(opts).encode())
     return h.hexdigest()
 
 

@@ -14,19 +14,34 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bcjr_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# BCJR_SANITIZE=1 (the CPU sanitizer run, tests/run_sanitizers.py) selects the build with
+# AddressSanitizer and UndefinedBehaviorSanitizer.
+_SANITIZE = os.environ.get("BCJR_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 _lib = None
 
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC"]
+# The sanitized build uses clang, whose sanitizer runtime the HIP library's sanitized build
+# (hipcc, i.e. clang) shares: one process cannot hold two sanitizer runtimes.
+_CLANG_DIR = "/opt/rocm/llvm"
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+def build(force: bool = True, sanitize: bool | None = None) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so`` (with ``sanitize``, with clang
+    and the address and undefined-behaviour sanitizers into ``oracle/liboracle_san.so``)."""
+    sanitize = _SANITIZE if sanitize is None else sanitize
+    path = os.path.join(_HERE, "liboracle_san.so" if sanitize else "liboracle.so")
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp"
+        if sanitize:
+            lib = os.path.join(_CLANG_DIR, "lib")
+            subprocess.check_call([os.path.join(_CLANG_DIR, "bin", "clang"), *_CFLAGS, *_SAN_FLAGS,
+                                   "-o", tmp, _SRC, "-lm", f"-L{lib}", f"-Wl,-rpath,{lib}"])
+        else:
+            subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, path)
+    return path
 
 
 def _load():
