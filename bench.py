@@ -143,8 +143,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--temp", type=float, default=None)
-    ap.add_argument("--history", choices=["full", "ckpt"], default="full",
-                    help="bitshift message histories: every step, or checkpoints + segment replay")
+    ap.add_argument("--history", choices=["full", "ckpt"], default=None,
+                    help="bitshift message histories: every step, or checkpoints + segment replay "
+                         "(default: checkpoints every 16 steps for the S = 65536 workload, as that "
+                         "configuration is specified; every step otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1536,
                     help="chains timed on the CPU oracle (at most CPU_SAMPLE_STATE_STEPS state-steps)")
@@ -631,6 +633,8 @@ def main():
     saved = torch.empty(bcjr.bcjr_saved_bytes(n, k, B, L), dtype=torch.uint8, device=dev)
     grad_w = torch.empty_like(w)
     grad_c = torch.empty_like(c)
+    if args.history is None:
+        args.history = "ckpt" if args.workload == 4 else "full"
     ck = args.history == "ckpt"
     wsf = bcjr.workspace(n, k, B, L, bcjr.FWD_CKPT if ck else bcjr.FWD, dev)
     wsb = bcjr.workspace(n, k, B, L, bcjr.BWD_CKPT if ck else bcjr.BWD, dev)
