@@ -50,9 +50,11 @@ constexpr int geom_block(int n, int k, int kind) {
 // Below this temperature the forward-backward carries its messages in fp64 (their fp32
 // rounding, which grows like 1/T, would put the gradient outside 1e-3). The fp64-message
 // backward needs both of a chain's message buffers (fp64 + fp32 per butterfly, single-buffered)
-// in LDS; shapes where they do not fit (S = 2^16 at k = 2) have no fp64-message kernels and the
-// entry points refuse temperatures below the threshold for them.
+// in LDS; shapes where they do not fit (S = 2^16 at k = 2) keep fp32 messages and form only the
+// emission in fp64 below the threshold, which meets the tolerances down to kMixedFloorT (at w
+// and c of unit scale); the entry points refuse lower temperatures for those shapes.
 constexpr float kPreciseBelowT = 0.01f;
+constexpr float kMixedFloorT = 0.004f;
 constexpr bool geom_precise_fits(int n, int k) {
   return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;
 }

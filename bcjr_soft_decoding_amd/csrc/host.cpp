@@ -102,10 +102,11 @@ bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, int kind,
 
 bool temp_ok(float T) { return isfinite(T) && T > 0.0f; }
 
-// Shapes without fp64-message kernels (geom_precise_fits false) keep fp32 messages, whose
-// rounding puts the gradient outside 1e-3 below kPreciseBelowT: refused there.
+// Shapes without fp64-message kernels (geom_precise_fits false) keep fp32 messages, with the
+// emission formed in fp64 below kPreciseBelowT; their gradient leaves 1e-3 below kMixedFloorT:
+// refused there.
 bool temp_supported(const bcjr_trellis* tr, float T) {
-  return T >= kPreciseBelowT || geom_precise_fits(tr->state_bits, tr->bits_per_step);
+  return T >= kMixedFloorT || geom_precise_fits(tr->state_bits, tr->bits_per_step);
 }
 
 // Workspaces are accessed with 16-byte vector loads and stores.

@@ -31,12 +31,22 @@ __device__ __forceinline__ float rcp_nr(float x) {
 // fp32 messages; emission -(u - v)^2 with u = q w, v = q c, q = sqrt(log2(e)/T).
 struct Fast {
   using MT = float;
-  static constexpr bool kPrecise = false;
+  static constexpr bool kPrecise = false;    // fp64 messages (and their lane geometry)
+  static constexpr bool kExactEmit = false;  // emission formed in fp64 from unscaled w and c
 };
 // fp64 messages; emission -kappa (w - c)^2 with kappa = log2(e)/T applied in fp64.
 struct Precise {
   using MT = double;
   static constexpr bool kPrecise = true;
+  static constexpr bool kExactEmit = true;
+};
+// fp32 messages with the emission formed as in Precise: w - c exactly, kappa (w - c)^2 and its
+// sum with the message offset in fp64, rounded to fp32 once. For shapes whose fp64 message
+// buffers do not fit LDS (the 2^16-state kernels) below kPreciseBelowT.
+struct Mixed {
+  using MT = float;
+  static constexpr bool kPrecise = false;
+  static constexpr bool kExactEmit = true;
 };
 
 // Per-call constants: per-state values v = sc * c, per-step u = sc * w, c = csc * v.
@@ -51,24 +61,24 @@ struct Consts {
 // enough to shift near-tied posteriors.
 template <class P>
 __device__ __forceinline__ typename P::MT emit(float u, float v, typename P::MT off, double kap) {
-  if constexpr (P::kPrecise) {
+  if constexpr (P::kExactEmit) {
     // (converted at each use: hoisted out of the step loop, the fp64 codebook values would
     // take twice the registers of the fp32 ones)
     float vv = v;
     asm volatile("" : "+v"(vv));
     const double dd = (double)u - (double)vv;
-    return __builtin_fma(-(kap * dd), dd, off);
+    return (typename P::MT)__builtin_fma(-(kap * dd), dd, (double)off);
   } else {
     (void)kap;
     const float d = u - v;
     return __builtin_fmaf(-d, d, off);
   }
 }
-// The scaled difference u - v = u - sc * c from a raw codebook value c, as one fma (with fp64
-// messages sc = 1, and this is u - c exactly), and the emission from it.
+// The scaled difference u - v = u - sc * c from a raw codebook value c, as one fma (with the
+// fp64 emission sc = 1, and this is u - c), and the emission from it.
 template <class P>
 __device__ __forceinline__ float sdiff(float u, float sc, float c) {
-  if constexpr (P::kPrecise) {
+  if constexpr (P::kExactEmit) {
     (void)sc;
     return u - c;
   } else {
@@ -76,11 +86,11 @@ __device__ __forceinline__ float sdiff(float u, float sc, float c) {
   }
 }
 // The emission from a raw codebook value: emit(u, sc * c) with the fp32 difference as one fma
-// (with fp64 messages sc = 1 and the difference is formed in fp64, as in emit).
+// (with the fp64 emission sc = 1 and the difference is formed in fp64, as in emit).
 template <class P>
 __device__ __forceinline__ typename P::MT emit_c(float u, float sc, float c, typename P::MT off,
                                                  double kap) {
-  if constexpr (P::kPrecise) {
+  if constexpr (P::kExactEmit) {
     (void)sc;
     return emit<P>(u, c, off, kap);
   } else {

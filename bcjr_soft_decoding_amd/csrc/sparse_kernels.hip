@@ -1637,7 +1637,7 @@ int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   using C = Cfg<(1 << k), geom_g(n, k, fwd_kind<P>()), geom_lps(n, k, fwd_kind<P>()), P, false>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
-  const Consts kc = make_consts(T, P::kPrecise);
+  const Consts kc = make_consts(T, P::kExactEmit);
   const size_t slot = sparse_fwd_slot_bytes(g, L, ckpt);
   const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
   double* slz = reinterpret_cast<double*>(saved);
@@ -1680,7 +1680,7 @@ int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   using C = Cfg<(1 << k), geom_g(n, k, bwd_kind<P>()), geom_lps(n, k, bwd_kind<P>()), P, true>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
-  const Consts kc = make_consts(T, P::kPrecise);
+  const Consts kc = make_consts(T, P::kExactEmit);
   const size_t slot = sparse_bwd_slot_bytes(g, L, ckpt);
   const long long seg = ckpt ? (long long)sparse_seg_len(L) : 0;
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + slot * (size_t)g.slots);
@@ -1725,12 +1725,16 @@ template <int n, int k>
 int run_fwd(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
             float T, float* w_hat, float* log_z, float* saved, void* ws, bool ckpt,
             hipStream_t st) {
-  if constexpr (precise_fits<n, k>())
+  if constexpr (precise_fits<n, k>()) {
     if (use_precise<n, k>(T)) {
       SparseGeom gp;
       if (!sparse_geom(n, k, B, kFwdP, &gp)) return (int)hipErrorInvalidValue;
       return run_fwd_p<n, k, Precise>(gp, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
     }
+  } else {
+    if (T < kPreciseBelowT)
+      return run_fwd_p<n, k, Mixed>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+  }
   return run_fwd_p<n, k, Fast>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
 }
 
@@ -1738,13 +1742,18 @@ template <int n, int k>
 int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
             float T, const float* saved, const float* gup, const float* hup, float* grad_w,
             float* grad_c, void* ws, bool ckpt, hipStream_t st) {
-  if constexpr (precise_fits<n, k>())
+  if constexpr (precise_fits<n, k>()) {
     if (use_precise<n, k>(T)) {
       SparseGeom gp;
       if (!sparse_geom(n, k, B, kBwdP, &gp)) return (int)hipErrorInvalidValue;
       return run_bwd_p<n, k, Precise>(gp, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws,
                                       ckpt, st);
     }
+  } else {
+    if (T < kPreciseBelowT)
+      return run_bwd_p<n, k, Mixed>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt,
+                                    st);
+  }
   return run_bwd_p<n, k, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt, st);
 }
 
@@ -1757,7 +1766,7 @@ int run_fwd_seg_p(const float* cb, const float* w, long long Bv, long long L, fl
   if (!sparse_geom(n, k, Bv, kind, &g)) return (int)hipErrorInvalidValue;
   using C = Cfg<(1 << k), geom_g(n, k, kind), geom_lps(n, k, kind), P, false>;
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
-  const Consts kc = make_consts(T, P::kPrecise);
+  const Consts kc = make_consts(T, P::kExactEmit);
   const size_t slot = BM == 2 ? 0 : sparse_fwd_slot_bytes(g, L, false);
   const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_fwd<C, false, BM>),
                                  C::BLOCK, g.slots);
@@ -1789,7 +1798,7 @@ int run_bwd_seg_p(const float* cb, const float* w, long long Bv, long long L, fl
   if (!sparse_geom(n, k, Bv, kind, &g)) return (int)hipErrorInvalidValue;
   using C = Cfg<(1 << k), geom_g(n, k, kind), geom_lps(n, k, kind), P, true>;
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
-  const Consts kc = make_consts(T, P::kPrecise);
+  const Consts kc = make_consts(T, P::kExactEmit);
   const size_t slot = BM == 2 ? 0 : sparse_bwd_slot_bytes(g, L, false);
   const int grid = resident_grid(reinterpret_cast<const void*>(&k_sparse_bwd<C, false, BM>),
                                  C::BLOCK, g.slots);

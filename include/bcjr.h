@@ -106,8 +106,11 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
  * Temperature and precision: below T = 0.01 the messages are carried in fp64 (their fp32
  * rounding grows like 1/T and would put the gradient outside 1e-3), above in fp32. The fp64
  * kernels exist for every state size whose backward message buffers fit the 160 KiB of LDS,
- * i.e. n <= 15 at k = 2; for n = 16 (S = 2^16) bcjr_forward and bcjr_backward return
- * BCJR_E_UNSUPPORTED when T < 0.01, before enqueueing anything (at T >= 0.01 they run).
+ * i.e. n <= 15 at k = 2. For n = 16 (S = 2^16) the messages stay fp32 and below T = 0.01 only
+ * the emission -(w - c)^2 / T and its sum with the message are formed in fp64 (w - c exactly),
+ * which keeps the tolerances down to T = 0.004 for w and c of unit scale (inputs of scale lam
+ * behave like unit-scale ones at T / lam^2); below T = 0.004 bcjr_forward and bcjr_backward
+ * return BCJR_E_UNSUPPORTED for n = 16, before enqueueing anything.
  */
 bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                          float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,
@@ -149,8 +152,9 @@ bcjr_status bcjr_forward_noalloc(const bcjr_trellis* tr, const float* w, int64_t
  * grad_codebook DEVICE [S] written (overwritten, summed over all B chains, fixed-order sum)
  * ws         DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 4) (checkpointed history) or
  *            >= bcjr_workspace_bytes(tr, B, L, 1) (full history)
- * Errors as bcjr_forward, including BCJR_E_UNSUPPORTED for S = 2^16 below T = 0.01 (there the
- * fp32-message gradient erred by up to 0.51 on an input with nearly tied paths).
+ * Errors as bcjr_forward, including BCJR_E_UNSUPPORTED for S = 2^16 below T = 0.004 (with the
+ * fp32 emission the gradient erred by up to 0.51 at T = 0.002 on an input with nearly tied
+ * paths; with the fp64 emission by 2.6e-4 there, and by 1.3e-3 on another input).
  */
 bcjr_status bcjr_backward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                           const void* saved, const float* grad_w_hat, const float* grad_log_z,

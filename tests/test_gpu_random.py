@@ -4,7 +4,7 @@ dense paths with random lengths, segment lengths and sizes. The cases are drawn 
 from fixed seeds, so every run checks the same ones. log Z is compared normwise like the other
 outputs: its fp32 error scales with the size of the summed terms, so a chain whose log Z happens
 to lie near zero would fail a purely relative test. At 2^16 states the library has no fp64-message
-kernels and refuses T below 0.01 (BCJR_E_UNSUPPORTED): those draws check the refusal."""
+kernels and refuses T below 0.004 (BCJR_E_UNSUPPORTED): such draws check the refusal."""
 import numpy as np
 import pytest
 import torch
@@ -70,7 +70,7 @@ def test_random_bitshift_shapes(n, B, L, T, ckpt, with_h, data_seed):
     w = (r.standard_normal((B, L)) * r.choice([0.3, 1.0, 2.0])).astype(np.float32)
     g = r.standard_normal((B, L)).astype(np.float32)
     h = r.standard_normal(B).astype(np.float32) if with_h else None
-    if n == 16 and T < 0.01:
+    if n == 16 and T < 0.004:
         assert_refused(n, 2, c, w, T, g)
         return
     ref = oracle.sparse_forward(n, 2, c, w, T)

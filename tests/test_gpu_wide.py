@@ -88,11 +88,11 @@ def test_wide_bitwise_deterministic(n, B, L, T):
             np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [0.0099, 0.004, 0.002])
-def test_2_16_states_below_001_refused(T):
+@pytest.mark.parametrize("T", [0.0039, 0.002, 0.001])
+def test_2_16_states_below_0004_refused(T):
     """The 2^16-state trellis has no fp64-message kernels (their two message buffers would not
-    fit LDS), and fp32 messages put the gradient outside 1e-3 on near-tied inputs below T = 0.01
-    (0.51 at T = 0.002 on one input): forward and backward refuse those temperatures with
+    fit LDS); with fp32 messages and the fp64 emission its gradient left 1e-3 at T = 0.002 on a
+    random input: forward and backward refuse temperatures below 0.004 with
     BCJR_E_UNSUPPORTED, enqueue nothing and leave their outputs untouched."""
     n, B, L = 16, 5, 24
     log_case(f"n=16 refused T={T}")
@@ -102,9 +102,32 @@ def test_2_16_states_below_001_refused(T):
     assert_refused(n, 2, c, w, T, g)
 
 
+@pytest.mark.parametrize("seed,B,L", [(7500, 5, 24), (7600, 6, 40)])
+@pytest.mark.parametrize("T", [0.0099, 0.006, 0.004])
+def test_2_16_states_below_001_fp64_emission(T, seed, B, L):
+    """Below T = 0.01 the 2^16-state kernels keep fp32 messages and form the emission in fp64
+    (w - c exactly, its square and its sum with the message in fp64). Against the oracle, both
+    histories, on the input whose gradient erred by 0.51 at T = 0.002 with the fp32 emission
+    (a near-tie between paths; seed 7500) and on a second one."""
+    n = 16
+    c = synth.normal(seed, (1 << n,))
+    w = synth.normal(seed + 1, (B, L))
+    g = synth.normal(seed + 2, (B, L))
+    h = synth.normal(seed + 3, (B,))
+    ref = oracle.sparse_forward(n, 2, c, w, T)
+    rb = oracle.sparse_backward(n, 2, c, w, T, g, h)
+    for hist in ("full", "ckpt"):
+        log_case(f"n=16 T={T} seed={seed} history={hist}")
+        got = _run(n, c, w, g, h, T, hist == "ckpt")
+        assert_normwise(got["w_hat"], ref["w_hat"], RTOL_FWD, f"{hist} w_hat")
+        assert_rel(got["log_z"], ref["log_z"], RTOL_FWD, f"{hist} log_z")
+        assert_normwise(got["grad_w"], rb["grad_w"], RTOL_GRAD, f"{hist} grad_w")
+        assert_normwise(got["grad_codebook"], rb["grad_codebook"], RTOL_GRAD, f"{hist} grad_c")
+
+
 def test_2_16_states_at_the_threshold_match_oracle():
-    """T = 0.01 exactly, the lowest temperature the 2^16-state kernels accept, against the oracle
-    on the input that erred by 0.51 at T = 0.002 with fp32 messages."""
+    """T = 0.01 exactly, the lowest temperature of the fp32 emission at 2^16 states, against the
+    oracle on the input that erred by 0.51 at T = 0.002 with the fp32 emission."""
     n, B, L, T = 16, 5, 24, 0.01
     c = synth.normal(7500, (1 << n,))
     w = synth.normal(7501, (B, L))
