@@ -29,7 +29,8 @@
 // large when T is small, so below T = 0.01 the messages are carried in fp64 and the emission
 // is formed from the unscaled difference w - c; exponentials, the posterior weights and the
 // conditional expectations stay fp32 in both policies. The 2^16-state trellis keeps fp32
-// messages at every T: its fp64 backward messages would not fit in LDS.
+// messages at every T (its fp64 backward messages would not fit in LDS) and below T = 0.01 forms
+// only the emission in fp64 (the Mixed policy).
 //
 // One persistent block per workspace slot loops over chain units. Phase A runs the forward
 // recursion and stores each lane's column offsets lam_t(x + a*NG) (the alpha-side inputs of
