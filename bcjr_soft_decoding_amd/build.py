@@ -30,6 +30,11 @@ FLAGS = [
 ]
 SOURCES = ["host.cpp", "sparse_kernels.hip", "viterbi_kernels.hip", "dense_kernels.hip", "code_kernels.hip",
            "scan_kernels.hip", "noalloc.hip"]
+# Second translation units: (source, object name, extra options). sparse_kernels.hip is built a
+# second time with only the shapes whose fp32-message kernels run faster under the machine
+# scheduler that maximises instruction-level parallelism (see ilp_fwd_shape / ilp_bwd_shape).
+ILP_FLAGS = ["-DBCJR_ILP_TU", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA_UNITS = [("sparse_kernels.hip", "sparse_kernels_ilp", ILP_FLAGS)]
 # The forward-backward kernels' max reductions need no NaN canonicalisation: a NaN or Inf input
 # still reaches the outputs through the exponentials and sums that follow every max (the
 # propagation the C ABI documents is tested); the Viterbi decoder keeps strict IEEE semantics
@@ -47,12 +52,13 @@ SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=und
              "-Xarch_host", "-g"]
 
 
-def _compile(src: str, sanitize: bool = False) -> str:
+def _compile(unit, sanitize: bool = False) -> str:
+    src, name, extra = unit if isinstance(unit, tuple) else (unit, unit, [])
     bdir = os.path.join(BUILD_DIR, "san") if sanitize else BUILD_DIR
-    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    obj = os.path.join(bdir, os.path.basename(name) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *(SAN_FLAGS if sanitize else []), *lang, "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *extra, *(SAN_FLAGS if sanitize else []), *lang,
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -69,7 +75,7 @@ def build(jobs: int = 8, sanitize: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     os.makedirs(os.path.join(BUILD_DIR, "san") if sanitize else BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+        objs = list(ex.map(lambda unit: _compile(unit, sanitize), [*SOURCES, *EXTRA_UNITS]))
     out = SAN_LIB if sanitize else LIB
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_FLAGS if sanitize else []), "-o",

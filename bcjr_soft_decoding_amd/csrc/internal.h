@@ -92,6 +92,14 @@ int launch_sparse_backward(const SparseGeom& g, const float* codebook, const flo
                            int64_t L, float T, const float* saved_logz2, const float* grad_w_hat,
                            const float* grad_log_z, float* grad_w, float* grad_codebook, void* ws,
                            bool ckpt, void* stream);
+// The fp32-message forward / backward of the shapes built in sparse_kernels.hip's second
+// translation unit (max-ILP scheduling); called by the launchers above for those shapes.
+int run_fwd_fast_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
+                     long long L, float T, float* w_hat, float* log_z, float* saved, void* ws,
+                     bool ckpt, void* stream);
+int run_bwd_fast_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
+                     long long L, float T, const float* saved, const float* gup, const float* hup,
+                     float* grad_w, float* grad_c, void* ws, bool ckpt, void* stream);
 int launch_fill_zero(float* dst, int64_t count, void* stream);
 // Grid of a persistent kernel: min(slots, resident blocks on the current device), or -1.
 int resident_grid(const void* kernel, int block, int64_t slots);

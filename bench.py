@@ -110,7 +110,7 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     opts = [build.ARCH, [f for f in build.FLAGS if not f.startswith("-I")],
-            build.EXTRA_FLAGS.get("sparse_kernels.hip", [])]
+            build.EXTRA_FLAGS.get("sparse_kernels.hip", []), build.ILP_FLAGS]
     h.update(repr(opts).encode())
     return h.hexdigest()
 
