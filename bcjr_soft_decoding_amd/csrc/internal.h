@@ -134,6 +134,13 @@ int launch_sparse_backward_seg(int mode, int n, int k, const float* codebook, co
                                const float* grad_w_hat, const float* grad_log_z, float* grad_w,
                                float* partial, void* ws, const SegLaunch& sl, int* grid_used,
                                void* stream);
+// The fp32 launches of launch_sparse_backward_seg for the shapes built in sparse_kernels.hip's
+// max-ILP translation unit.
+int launch_sparse_backward_seg_ilp(int mode, int n, int k, const float* codebook, const float* w,
+                                   int64_t Bv, int64_t L, float T, const float* w_hat,
+                                   const float* grad_w_hat, const float* grad_log_z, float* grad_w,
+                                   float* partial, void* ws, const SegLaunch& sl, int* grid_used,
+                                   void* stream);
 // out[s] = sum over slots of partial[slot][s], slots in order.
 int launch_reduce_slots(const float* partial, int64_t slots, int S, float* out, void* stream);
 bool scan_shape_built(int n, int k);
