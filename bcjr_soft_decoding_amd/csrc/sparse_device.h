@@ -309,6 +309,43 @@ __device__ __forceinline__ void load_hist(const T* __restrict__ src, T* dst) {
   }
 }
 
+// A history row pointer in the global address space, made to depend on the values v (no
+// instruction): a load through it cannot be issued before v is computed. The phase-B history
+// loads replace registers whose last use is in v; hoisted above it they would need registers of
+// their own and a copy every step. (Kept global: a generic pointer would turn the loads into
+// flat loads, which LDS waits would then also wait for.)
+template <class T>
+using gptr = const __attribute__((address_space(1))) T*;
+template <int N, class T, class V>
+__device__ __forceinline__ gptr<T> after(gptr<T> p, const V (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm("" : "+v"(p) : "v"(v[i]));
+  return p;
+}
+template <class T>
+__device__ __forceinline__ gptr<T> global(const T* p) {
+  return (gptr<T>)p;
+}
+
+// Waits for every outstanding vector memory access (s_waitcnt vmcnt(0); the expcnt and lgkmcnt
+// fields at their maxima). Before a loop whose history loads are waited for by count, so that
+// loads issued ahead of it in another order do not make those counts cover the younger loads.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Values [off, off + N) of a lane's history row (whole 16-byte chunks), as load_hist.
+template <int N, int BLK, class T>
+__device__ __forceinline__ void load_hist_part(gptr<T> src, int off, T* dst) {
+  constexpr int V = 16 / (int)sizeof(T);
+  static_assert(N % V == 0, "whole 16-byte chunks");
+  using Vec = __attribute__((ext_vector_type(V))) T;
+#pragma unroll
+  for (int i = 0; i < N; i += V) {
+    const Vec x = __builtin_nontemporal_load((gptr<Vec>)(src + (size_t)((off + i) / V) * BLK * V));
+#pragma unroll
+    for (int j = 0; j < V; ++j) dst[i + j] = x[j];
+  }
+}
+
 // The same copies with the non-temporal hint, for the 1024-lane backward's history streams
 // (written once, read once or twice a whole chain later): they then do not push the codebook,
 // which every block rereads each step, out of L2 (measured 4% faster at S = 65536).

@@ -297,6 +297,12 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
         for (int r = 0; r < K; ++r) rr[g][r] = (MT)0;
     }
+    // Per-step outputs of a chain are kept by lane t mod LPS and written together when that
+    // lane's value for step t is in (t mod LPS == 0): the phase-B loop then issues no vector
+    // store on most steps, so its waits for each block's history loads count only those loads
+    // (a store in every step, issued by one lane under a branch, made the compiler's wait counts
+    // cover the next blocks' loads too).
+    float whs = 0.f;
     const long long nseg = seg ? ncp : 1;
     for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
       const long long t0 = seg ? sgi * seg : 0;
@@ -310,24 +316,24 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         }
       }
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
-      MT lcn[G][K];
-      load_hist<KG, BLOCK>(hist(entry(t1 - 1)), &lcn[0][0]);
+      // lam offsets of the step being processed: each block's are replaced by the previous
+      // step's right after their last use, so the loads have a step to land and need no
+      // registers of their own (loaded a step ahead, they would be copied every step)
+      MT lcur[G][K];
+      load_hist<KG, BLOCK>(hist(entry(t1 - 1)), &lcur[0][0]);
       double Nn = ns[(t1 - 1) * SPB + q];
+      wait_vm0();
       for (long long t = t1 - 1; t >= t0; --t) {
-        MT lcur[G][K];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int a = 0; a < K; ++a) lcur[g][a] = lcn[g][a];
-        const double Nt = Nn;
-        {  // unconditional (at the segment's first step it re-reads step t): a conditional load
-           // makes the compiler copy the carried rows out and back every step
-          const long long tp = t > t0 ? t - 1 : t;
-          load_hist<KG, BLOCK>(hist(entry(tp)), &lcn[0][0]);
-          Nn = ns[tp * SPB + q];
-        }
+        // unconditional (at the segment's first step the loads re-read step t): a conditional
+        // load makes the compiler copy the carried rows out and back every step
+        const long long tp = t > t0 ? t - 1 : t;
         const float u = k.sc * wb[t];
-        const MT LZ = (MT)((lz2 - Nt) - Np);
+        const MT LZ = (MT)((lz2 - Nn) - Np);
+        Nn = ns[tp * SPB + q];
+        // (issued before the step's history loads, so that the next step's wait for it does not
+        // also wait for them)
+        __builtin_amdgcn_sched_barrier(0);
+        gptr<MT> hn = global(hist(entry(tp)));
         float num = 0.f, den = 0.f;
         MT mx = (MT)-INFINITY;
         MT rout[G][K];
@@ -335,6 +341,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int g = 0; g < G; ++g) {
           float Vg[K][K];
           vsrc.get(g, Vg);
+          float fa[K];
 #pragma unroll
           for (int a = 0; a < K; ++a) {
             MT y[K];
@@ -355,9 +362,12 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             rout[g][a] = m + (MT)lg2(cs);
             mx = tmax(mx, rout[g][a]);
             const float f = ex2((float)((m + lcur[g][a]) - LZ));
+            fa[a] = f;
             num = __builtin_fmaf(f, cw, num);
             den = __builtin_fmaf(f, cs, den);
           }
+          hn = after(hn, fa);
+          load_hist_part<K, BLOCK>(hn, g * K, lcur[g]);
         }
         MT* mw = msg[mb] + q * M;
         if (t > 0) {
@@ -368,10 +378,18 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         }
         MT v3[3] = {(MT)num, (MT)den, mx};
         chain_reduce<C, 3, 4u>(v3, red, rp);
-        if (valid && p == 0) {
+        {  // kept by lane t mod LPS, written once per LPS steps (step_out)
           const float wh = ((float)v3[0] / (float)v3[1]) * k.csc;
-          w_hat[wofs + t] = wh;
-          if constexpr (BM == 0) saved_what[b * L + t] = wh;
+          if (p == (int)(t % LPS)) whs = wh;
+          if (t % LPS == 0) {
+            // (the lane offset is formed here: folded into the addresses by the loop's strength
+            // reduction, it would keep two 64-bit address registers per lane live all along)
+            const unsigned lane = opaque((unsigned)p);
+            if (valid && t + lane < L) {
+              w_hat[wofs + t + lane] = whs;
+              if constexpr (BM == 0) saved_what[b * L + t + lane] = whs;
+            }
+          }
         }
         if (t == 0) break;
         const MT sh = floor(v3[2]);
@@ -959,6 +977,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
 #pragma unroll
         for (int r = 0; r < K; ++r) { rr[g][r] = (MT)0; qr[g][r] = 0.f; }
     }
+    float gws = 0.f;  // grad_w of step t, kept by lane t mod LPS (as w_hat in k_sparse_fwd)
     const long long nseg = seg ? ncp : 1;
     for (long long sgi = nseg - 1; sgi >= 0; --sgi) {
       const long long t0 = seg ? sgi * seg : 0;
@@ -974,32 +993,27 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         }
       }
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
-      MT lcn[G][K];
-      float pcn[G][K];
-      load_hist<KG, BLOCK>(histl(entry(t1 - 1)), &lcn[0][0]);
-      load_hist<KG, BLOCK>(histp(entry(t1 - 1)), &pcn[0][0]);
+      // lam and Phi offsets of the step being processed, each block's replaced by the previous
+      // step's right after their last use (as in k_sparse_fwd)
+      MT lcur[G][K];
+      float pcur[G][K];
+      load_hist<KG, BLOCK>(histl(entry(t1 - 1)), &lcur[0][0]);
+      load_hist<KG, BLOCK>(histp(entry(t1 - 1)), &pcur[0][0]);
       double Nn = ns[(t1 - 1) * SPB + q];
+      wait_vm0();
       for (long long t = t1 - 1; t >= t0; --t) {
-        MT lcur[G][K];
-        float pcur[G][K];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int a = 0; a < K; ++a) { lcur[g][a] = lcn[g][a]; pcur[g][a] = pcn[g][a]; }
-        const double Nt = Nn;
-        {  // unconditional (at the segment's first step it re-reads step t): a conditional load
-           // makes the compiler copy the carried rows out and back every step
-          const long long tp = t > t0 ? t - 1 : t;
-          load_hist<KG, BLOCK>(histl(entry(tp)), &lcn[0][0]);
-          load_hist<KG, BLOCK>(histp(entry(tp)), &pcn[0][0]);
-          Nn = ns[tp * SPB + q];
-        }
+        // unconditional (at the segment's first step the loads re-read step t), as in k_sparse_fwd
+        const long long tp = t > t0 ? t - 1 : t;
         const float u = k.sc * wb[t];
         const float gt = gb[t];
         const float gtp = gt * k.csc;
         const float gtk = gt * ik2;
         const float gwh = gt * whb[t];
-        const MT LZ = (MT)((lz2 - Nt) - Np);
+        const MT LZ = (MT)((lz2 - Nn) - Np);
+        Nn = ns[tp * SPB + q];
+        __builtin_amdgcn_sched_barrier(0);  // (as in k_sparse_fwd)
+        gptr<MT> hln = global(histl(entry(tp)));
+        gptr<float> hpn = global(histp(entry(tp)));
         float qrc[G][K];  // Psi_t - g_t w_hat_t at the row offsets
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -1016,6 +1030,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int g = 0; g < G; ++g) {
           float Vg[K][K];
           vsrc.get(g, Vg);
+          float fa[K], pv[K];
 #pragma unroll
           for (int a = 0; a < K; ++a) {
             MT y[K];
@@ -1044,6 +1059,8 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             mx = tmax(mx, rout[g][a]);
             const float f = ex2((float)((m + lcur[g][a]) - LZ));
             const float pa = pcur[g][a] + hx;
+            fa[a] = f;
+            pv[a] = pa;
             xs = __builtin_fmaf(f, __builtin_fmaf(pa, cs, ps), xs);
             // (a uniform branch per 4x4 block: it also bounds the live ranges the scheduler
             // builds across blocks, which keeps this kernel at two waves per SIMD)
@@ -1057,6 +1074,10 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
               }
             }
           }
+          hln = after(hln, fa);
+          hpn = after(hpn, pv);
+          load_hist_part<K, BLOCK>(hln, g * K, lcur[g]);
+          load_hist_part<K, BLOCK>(hpn, g * K, pcur[g]);
         }
         MT* mw = msgl[mb] + q * M;
         float* pw = msgp[mb] + q * M;
@@ -1072,8 +1093,14 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         MT v2[3] = {(MT)gw, mx, (MT)xs};
         chain_reduce<C, 3, 2u>(v2, red, rp);
         xbar += (float)v2[2] - h;
-        if (valid && p == 0)
-          grad_w[wofs + t] = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+        {  // kept by lane t mod LPS and written once per LPS steps, as w_hat in k_sparse_fwd
+          const float gwt = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
+          if (p == (int)(t % LPS)) gws = gwt;
+          if (t % LPS == 0) {
+            const unsigned lane = opaque((unsigned)p);  // (as in k_sparse_fwd)
+            if (valid && t + lane < L) grad_w[wofs + t + lane] = gws;
+          }
+        }
         if (t == 0) break;
         const MT sh = floor(v2[1]);
 #pragma unroll
