@@ -21,12 +21,6 @@ constexpr double kLog2e = 1.4426950408889634074;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
-// Reciprocal refined by one Newton step: the conditional expectations below are weighted
-// averages carried along the whole chain, so the weights must sum to one to within rounding.
-__device__ __forceinline__ float rcp_nr(float x) {
-  const float r = __builtin_amdgcn_rcpf(x);
-  return __builtin_fmaf(__builtin_fmaf(-x, r, 1.0f), r, r);
-}
 
 // fp32 messages; emission -(u - v)^2 with u = q w, v = q c, q = sqrt(log2(e)/T).
 struct Fast {
@@ -48,6 +42,18 @@ struct Mixed {
   static constexpr bool kPrecise = false;
   static constexpr bool kExactEmit = true;
 };
+
+// 1/x for the sums of a softmax (x in [1, K]) that normalise the conditional expectations'
+// weights. v_rcp_f32 is within 0.88 ulp of 1/x over [1, 4) (all 2^24 inputs, measured on
+// MI355X; mean -0.07 ulp); with fp32 messages and emission, whose rounding at the message
+// magnitudes is far larger, it is used as is. The policies with the fp64 emission (the lowest
+// temperatures) refine it by one Newton step, to the correctly rounded quotient.
+template <class P>
+__device__ __forceinline__ float rcp_w(float x) {
+  const float r = __builtin_amdgcn_rcpf(x);
+  if constexpr (P::kExactEmit) return __builtin_fmaf(__builtin_fmaf(-x, r, 1.0f), r, r);
+  return r;
+}
 
 // Per-call constants: per-state values v = sc * c, per-step u = sc * w, c = csc * v.
 struct Consts {

@@ -854,7 +854,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
             ph = __builtin_fmaf(e, __builtin_fmaf(gtp, Vg[r][a], pcc[g][a]), ph);
           }
           out[g][r] = m + (MT)lg2(s);
-          pout[g][r] = ph * rcp_nr(s);
+          pout[g][r] = ph * rcp_w<P>(s);
           mx = tmax(mx, out[g][r]);
         }
       }
@@ -1055,7 +1055,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
               ps = __builtin_fmaf(e[r], t2[r], ps);
             }
             rout[g][a] = m + (MT)lg2(cs);
-            qout[g][a] = ps * rcp_nr(cs);
+            qout[g][a] = ps * rcp_w<P>(cs);
             mx = tmax(mx, rout[g][a]);
             const float f = ex2((float)((m + lcur[g][a]) - LZ));
             const float pa = pcur[g][a] + hx;
@@ -1317,7 +1317,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             ph = __builtin_fmaf(ea, __builtin_fmaf(gt, Vg[a][r], pcc[a]), ph);
           }
           lo[g][r] = m + (MT)lg2(s);
-          po[g][r] = ph * rcp_nr(s);
+          po[g][r] = ph * rcp_w<P>(s);
           pin(lo[g][r]);
           pin(po[g][r]);
           mx = tmax(mx, lo[g][r]);
@@ -1542,7 +1542,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
               ps = __builtin_fmaf(e4[r], t2[r], ps);
             }
             ro[g][a] = m + (MT)lg2(cs);
-            qo[g][a] = ps * rcp_nr(cs);
+            qo[g][a] = ps * rcp_w<P>(cs);
             pin(ro[g][a]);
             pin(qo[g][a]);
             mx = tmax(mx, ro[g][a]);
