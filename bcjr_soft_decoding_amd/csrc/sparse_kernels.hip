@@ -163,7 +163,7 @@ k_sparse_fwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
     // One forward step: the column offsets lc of step t -> those of step t + 1 (t < L - 1).
     auto advance = [&](long long t) {
       const float u = k.sc * wnx;
-      wnx = wb[t + 1 < L ? t + 1 : t];
+      wnx = wb[t != L - 1 ? t + 1 : t];  // (t < L: a scalar 64-bit compare)
       MT out[G][K];
       MT mx = (MT)-INFINITY;
 #pragma unroll
@@ -501,7 +501,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
     // the offsets as history entry e (e >= 0) and returns the outputs' chain-wide maximum.
     auto fstep = [&](long long t, long long e) -> MT {
       const float u = k.sc * wn;
-      wn = vload(wb, t + 1 < L ? t + 1 : t);
+      wn = vload(wb, t != L - 1 ? t + 1 : t);
       const MT* __restrict__ src = msg[cur];
       MT* __restrict__ dst = msg[cur ^ 1];
       MT mx = (MT)-INFINITY;
@@ -823,7 +823,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       const float u = k.sc * wn;
       const float gtp = gn * k.csc;     // g_t c(s) = gtp * v(s)
       const float gwh = gn * hn;        // g_t w_hat_t
-      inputs_at(t + 1 < L ? t + 1 : t);
+      inputs_at(t != L - 1 ? t + 1 : t);  // (as in k_sparse_fwd)
       MT out[G][K];
       float pout[G][K];
       float pcc[G][K];  // Phi_t - g_t w_hat_t at the column offsets
@@ -1275,7 +1275,7 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       const float u = k.sc * wn;
       const float gt = gn;           // g_t c(s) from the raw codebook value
       const float gwh = gn * whn;    // g_t w_hat_t
-      steps_from(t + 1 < L ? t + 1 : t);
+      steps_from(t != L - 1 ? t + 1 : t);
       MT lo[G][K];
       float po[G][K];
       MT mx = (MT)-INFINITY;

@@ -111,6 +111,18 @@ def test_edge_shapes(n, B, L):
     _compare(n, 2, c, w, 0.2, g, None, "edge")
 
 
+# The per-step outputs (w_hat, grad_w) are kept by lane t mod LPS of a chain and written once
+# per LPS steps: lengths with several windows and a partial first one, at the geometries of
+# one-wave (LPS 64 forward), two-wave (LPS 128 backward) and four-wave (LPS 256) chains.
+@pytest.mark.parametrize("n,B,L", [(12, 3, 129), (12, 2, 257), (13, 2, 300), (11, 4, 95),
+                                   (10, 5, 65)])
+def test_output_windows(n, B, L):
+    c = synth.normal(720 + n, (1 << n,))
+    w = synth.normal(820 + n + L, (B, L))
+    g = synth.normal(920 + n + L, (B, L))
+    _compare(n, 2, c, w, 0.15, g, None, "windows")
+
+
 def test_zero_chains_is_a_no_op():
     c = dev(synth.codebook(2))
     w = torch.empty((0, 16), dtype=torch.float32, device="cuda")
