@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "geom.h"
 #include "internal.h"
 
@@ -409,6 +411,24 @@ __device__ __forceinline__ unsigned opaque(unsigned x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// base + a lane's element offset, formed as a block-uniform base plus an opaque 32-bit byte
+// offset: the form the scalar-base global addressing takes (SGPR pair + 32-bit VGPR offset), so
+// no 64-bit address is added per use. (With the element index itself opaque, its scaling to bytes
+// is a 64-bit offset that addressing cannot take, and every use costs a 64-bit add.)
+// The base (the same in every lane) is read into scalar registers first, so that the compiler
+// does not fold part of it into a per-lane 64-bit sum.
+template <class T>
+__device__ __forceinline__ T* at_lane(T* base, unsigned elem) {
+  using GB = typename std::conditional<std::is_const<T>::value,
+                                       const __attribute__((address_space(1))) char,
+                                       __attribute__((address_space(1))) char>::type;
+  const unsigned long long a = (unsigned long long)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  GB* b = (GB*)(((unsigned long long)hi << 32) | lo);
+  return (T*)(b + opaque(elem * (unsigned)sizeof(T)));
+}
+
 // A per-step scalar read through the vector memory path, behind a zero offset the compiler
 // cannot see through. A scalar load shares its completion counter with LDS accesses, and scalar
 // loads complete out of order, so the first LDS wait after a scalar load issued a step ahead

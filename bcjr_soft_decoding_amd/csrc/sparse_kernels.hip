@@ -448,7 +448,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
 #pragma unroll
     for (int a = 0; a < K; ++a) {
       const float* __restrict__ ub = cb + (g * K * LPS + a * M);
-      load_vec<K>(ub + opaque(lo4), c[a]);
+      load_vec<K>(at_lane(ub, lo4), c[a]);
     }
   };
   struct FIn {  // inputs of a forward block loaded ahead
@@ -465,9 +465,11 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   char* sb = static_cast<char*>(ws) + (size_t)blockIdx.x * slot_bytes;
   MT* __restrict__ hs = reinterpret_cast<MT*>(sb);
   double* __restrict__ ns = reinterpret_cast<double*>(sb + (size_t)nh * LPS * KG * 8);
-  // history entries are block-major, [H][G][LPS][K]: block g of this lane in entry e is at
-  // hist(e) + g*LPS*K
-  auto hist = [&](long long e) { return hs + (size_t)e * LPS * KG + opaque(lo4); };
+  // history entries are block-major, [H][G][LPS][K]: hist(e, g) is block g of this lane in
+  // entry e
+  auto hist = [&](long long e, int g) {
+    return at_lane(hs + (size_t)e * LPS * KG + (size_t)g * (LPS * K), lo4);
+  };
   int rp = 0;
 
   // units == B (one chain per unit), so every unit is a chain
@@ -489,7 +491,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         MT lc[K];
 #pragma unroll
         for (int a = 0; a < K; ++a) lc[a] = msg[cur][p + g * LPS + a * NG] - sh;
-        store_vec<K>(hist(e) + g * (LPS * K), lc);
+        store_vec<K>(hist(e, g), lc);
       }
     };
     // Loaded ahead of their use: the next block's raw codebook values (block 0 when a run of
@@ -511,7 +513,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
             MT lc[K];
 #pragma unroll
             for (int a = 0; a < K; ++a) lc[a] = src[p + g * LPS + a * NG] - sh;
-            if (e >= 0) store_vec<K>(hist(e) + g * (LPS * K), lc);
+            if (e >= 0) store_vec<K>(hist(e, g), lc);
             MT out[K];
 #pragma unroll
             for (int r = 0; r < K; ++r) {
@@ -589,7 +591,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
         __syncthreads();
         MT c0[KG];
 #pragma unroll
-        for (int g = 0; g < G; ++g) load_vec<K>(hist(sgi) + g * (LPS * K), c0 + g * K);
+        for (int g = 0; g < G; ++g) load_vec<K>(hist(sgi, g), c0 + g * K);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -612,7 +614,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
       auto entry = [&](long long t) { return seg ? ncp + (t - t0) : t; };
       BIn ba, bb;  // block-ahead loads, two register sets in turn
       cblock(0, ba.c);
-      load_vec<K>(hist(entry(t1 - 1)), ba.l);
+      load_vec<K>(hist(entry(t1 - 1), 0), ba.l);
       // the step's scalars, loaded a step ahead (a load consumed at once would also wait for
       // the stores issued before it)
       double nsn = ns[t1 - 1];
@@ -637,7 +639,7 @@ k_sparse_fwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
               // re-reads an entry of the segment)
               cblock(gn < G ? gn : 0, in.c);
               const long long en = gn < G ? entry(t) : entry(t > t0 ? t - 1 : t);
-              load_vec<K>(hist(en) + (gn < G ? gn : 0) * (LPS * K), in.l);
+              load_vec<K>(hist(en, gn < G ? gn : 0), in.l);
             },
             [&](int g, const BIn& in) {
               MT rr[K];
