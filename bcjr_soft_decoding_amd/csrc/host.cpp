@@ -242,7 +242,8 @@ bcjr_status bcjr_backward_scan(const bcjr_trellis* tr, const float* w, int64_t B
                            reinterpret_cast<double*>(base + plan.rho1),
                            reinterpret_cast<double*>(base + plan.sc0),
                            reinterpret_cast<float*>(base + plan.phi0),
-                           reinterpret_cast<float*>(base + plan.psi1), stream);
+                           reinterpret_cast<float*>(base + plan.psi1), slots,
+                           plan.bytes - plan.slots, stream);  // (the slots are free in phase 2)
   // phase 3: every segment's gradient from its boundary values, then the codebook partials
   g1 = g2 = 0;
   if (e == 0)
@@ -308,7 +309,7 @@ bcjr_status bcjr_forward_scan(const bcjr_trellis* tr, const float* w, int64_t B,
   // phase 2: boundary messages by a scan over the segments
   if (e == 0)
     e = launch_scan_bounds(rows, rscale, nullptr, B, plan.ptot, M, lam0, rho1, sc0, nullptr,
-                           nullptr, stream);
+                           nullptr, slots, plan.bytes - plan.slots, stream);  // (slots free here)
   // phase 3: every segment's forward-backward from its boundary messages
   if (e == 0) {
     SegLaunch sl{plan.pmain, 0, plan.seg, L, plan.ptot, lam0, rho1, sc0, nullptr, nullptr};

@@ -141,30 +141,57 @@ int launch_sparse_backward_seg_ilp(int mode, int n, int k, const float* codebook
                                    const float* grad_w_hat, const float* grad_log_z, float* grad_w,
                                    float* partial, void* ws, const SegLaunch& sl, int* grid_used,
                                    void* stream);
-// out[s] = sum over slots of partial[slot][s], slots in order.
-int launch_reduce_slots(const float* partial, int64_t slots, int S, float* out, void* stream);
+// out[s] = sum over slots of partial[slot][s] in a fixed order (partial is scratch: overwritten).
+int launch_reduce_slots(float* partial, int64_t slots, int S, float* out, void* stream);
 bool scan_shape_built(int n, int k);
-// Boundary scan; with frows (moment rows) also the conditional expectations phi0 / psi1.
+// Boundary scan; with frows (moment rows) also the conditional expectations phi0 / psi1. With
+// enough segments and M <= 64 it runs as a tree over the segments in tree_ws (scratch of
+// tree_ws_bytes bytes, free during the call; null: the sequential scan).
 int launch_scan_bounds(const float* rows, const double* rscale, const float* frows, int64_t chains,
                        int64_t ptot, int M, double* lam0, double* rho1, double* sc0, float* phi0,
-                       float* psi1, void* stream);
+                       float* psi1, void* tree_ws, size_t tree_ws_bytes, void* stream);
+
+// The boundary scan runs as a tree over the segments (scan_kernels.hip) for M <= 64 from this
+// many segments on; below it the sequential scan's few steps cost less than the tree's launches.
+constexpr int64_t kTreeMinSegments = 64;
+// Bytes of the tree's scratch for `chains` chains of `ptot` segments: per level above the
+// segments, the composed matrices (and moment matrices), row scales and both boundary vectors
+// (and expectations) of every node; 0 where the sequential scan runs.
+inline size_t scan_tree_bytes(int64_t chains, int64_t ptot, int64_t M, bool mom) {
+  if (M > 64 || ptot < kTreeMinSegments) return 0;
+  size_t b = 0;
+  for (int64_t n = (ptot + 1) / 2;; n = (n + 1) / 2) {
+    const size_t nodes = (size_t)chains * (size_t)n;
+    b += round256(nodes * (size_t)M * (size_t)M * sizeof(float)) * (mom ? 2 : 1);
+    b += round256(nodes * (size_t)M * sizeof(double)) * 3;
+    if (mom) b += round256(nodes * (size_t)M * sizeof(float)) * 2;
+    if (n == 1) break;
+  }
+  return b;
+}
 
 constexpr int64_t kScanMinSeg = 16;
 
-// Default segment length. A chain's time is about P * t2 (the boundary scan, sequential over
-// its P = L / seg segments) + seg * t3 (each segment's own sweeps, sequential in its steps),
+// Default segment length. A chain's time is about P * t2 (the boundary scan over its
+// P = L / seg segments) + seg * t3 (each segment's own sweeps, sequential in its steps),
 // smallest at seg = sqrt(L * t2 / t3). Measured on MI355X: t3 = 1.5 us per step (forward and
-// backward sweep of one chain, with the segment geometry kFwdS / kBwdS); per scan step
-// t2 = 1.0 us + 0.03 us * M for M = S/K <= 64 (one wave per chain and direction) and
-// 2.5 us + 3.7e-4 us * M^2 above (one block).
+// backward sweep of one chain, with the segment geometry kFwdS / kBwdS). The sequential scan
+// costs t2 = 1.0 us + 0.03 us * M per segment for M = S/K <= 64 (one wave per chain and
+// direction) and 2.5 us + 3.7e-4 us * M^2 above (one block). The tree over the segments
+// (M <= 64, from kTreeMinSegments segments) costs about t2 = 0.0015 us * M * B per segment
+// (fitted to segment-length sweeps at S = 16, 64, 256 with B = 1, 2, 16 chains of 2^16..2^20
+// steps, whose optima it places within 1.3x), so where it applies its optimum is used.
 // A segment shorter than the others (when seg does not divide L) runs in launches of its own
 // after the others, so the default prefers a divisor of L within 1.5x of that optimum, else
 // seg = floor(L / P) for P = ceil(L / optimum), which keeps the short segment under P steps.
 inline int64_t scan_default_seg(int n, int k, int64_t B, int64_t L) {
-  (void)B;
   const double M = (double)(((int64_t)1 << n) >> k);
-  const double t2 = M <= 64 ? 1.0 + 0.03 * M : 2.5 + 3.7e-4 * M * M, t3 = 1.5;
-  const double opt = sqrt((double)L * t2 / t3);
+  const double t3 = 1.5;
+  double opt = sqrt((double)L * (M <= 64 ? 1.0 + 0.03 * M : 2.5 + 3.7e-4 * M * M) / t3);
+  if (M <= 64) {
+    const double tree = sqrt((double)L * 0.0015 * M * (double)(B > 1 ? B : 1) / t3);
+    if ((double)L / tree >= (double)kTreeMinSegments) opt = tree;
+  }
   if (opt <= (double)kScanMinSeg) return kScanMinSeg;
   if (opt >= (double)L) return L;
   const int64_t lo = (int64_t)ceil(opt / 1.5), hi = (int64_t)floor(opt * 1.5);
@@ -207,6 +234,9 @@ inline void scan_plan(const SparseGeom& gmain, const SparseGeom& gtail, int n, i
     const size_t b = sparse_fwd_ws_bytes(gtail, p->tail, false);
     if (b > a) a = b;
   }
+  // the boundary scan's tree uses the same region (free between the segment launches)
+  const size_t tb = scan_tree_bytes(B, p->ptot, M, false);
+  if (tb > a) a = tb;
   p->bytes = p->slots + round256(a);
 }
 
@@ -238,6 +268,8 @@ inline void scan_plan_bwd(const SparseGeom& gmain, const SparseGeom& gtail, int6
     const size_t b = sparse_bwd_ws_bytes(gtail, p->tail, false);
     if (b > a) a = b;
   }
+  const size_t tb = scan_tree_bytes(B, p->ptot, M, true);  // (as in scan_plan)
+  if (tb > a) a = tb;
   p->bytes = p->slots + round256(a);
 }
 

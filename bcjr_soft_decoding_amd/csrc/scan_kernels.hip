@@ -371,15 +371,268 @@ k_scan_wave(const float* __restrict__ rows, const double* __restrict__ rscale,
 #undef BCJR_WAVE_LOAD
 }
 
+// ---------------------------------------------------------------------------------------------
+// The same boundary vectors (and expectations) by a binary tree over a chain's segments, for
+// M <= 64 and chains of many segments. The scan's steps are associative: node i of level l
+// covers segments [i 2^l, (i + 1) 2^l) (clipped to the chain) and holds their composed transfer
+// matrix, C = C_left (x) C_right in the (log-sum-exp, +) semiring, with, for the moments, the
+// composed moment matrix F_C(a, b) = sum_k w(a, k, b) (F_left(a, k) + F_right(k, b)), w the
+// softmax weights of C(a, b)'s log-sum-exp. The vectors then come down the tree from the root
+// (free start and free end: 0): the forward vector at the start of a node's right child is the
+// one at the node's start times the left child's product, the backward vector at the end of its
+// left child the right child's product times the one at the node's end. Depth log2 P instead of P
+// sequential steps, for M times the arithmetic of the scan (a product costs M^3 terms where a
+// step costs M^2). Composed matrices keep the rows' form: fp32 offsets <= 0 and double row
+// scales. A node without a right child is its left child.
+// ---------------------------------------------------------------------------------------------
+template <int M>
+struct TreeGeo {
+  static constexpr int TPB = M * M < 1024 ? M * M : 1024;  // threads per product
+  static constexpr int TPR = TPB / M;                       // threads per output row
+  static constexpr int CPT = M / TPR;                       // columns per thread (consecutive)
+  static constexpr int RS = M + 4;                          // LDS row stride (16-byte aligned)
+  static_assert(TPR <= 64 && (64 % TPR) == 0 && CPT * TPR == M, "tree product geometry");
+};
+
+template <int W, class T>
+__device__ __forceinline__ T group_max(T v) {
+  for (int o = 1; o < W; o <<= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+
+// One product per block: parent node `node` of level (np nodes per chain) from children 2i and
+// 2i + 1 of the level below (nc nodes per chain).
+template <int M, bool MOM>
+__global__ void __launch_bounds__(TreeGeo<M>::TPB)
+k_tree_compose(const float* __restrict__ cq, const double* __restrict__ crs,
+               const float* __restrict__ cf, long long nc, float* __restrict__ pq,
+               double* __restrict__ prs, float* __restrict__ pf, long long np) {
+  using G = TreeGeo<M>;
+  constexpr int RS = G::RS, TPR = G::TPR, CPT = G::CPT;
+  __shared__ __attribute__((aligned(16))) float qb[M * RS];
+  __shared__ __attribute__((aligned(16))) float fb[MOM ? M * RS : 4];
+  __shared__ float br[M * RS];
+  __shared__ float fa[MOM ? M * RS : 1];
+  __shared__ double rsb[M];
+  const long long node = blockIdx.x;
+  const long long ch = node / np, i = node % np;
+  const long long left = ch * nc + 2 * i;
+  const int t = threadIdx.x;
+  const float* __restrict__ aq = cq + left * (M * M);
+  const double* __restrict__ ars = crs + left * M;
+  float* __restrict__ oq = pq + node * (M * M);
+  if (2 * i + 1 >= nc) {  // no right child: the node is its left child
+    for (int e = t; e < M * M; e += G::TPB) {
+      oq[e] = aq[e];
+      if constexpr (MOM) pf[node * (M * M) + e] = cf[left * (M * M) + e];
+    }
+    for (int e = t; e < M; e += G::TPB) prs[node * M + e] = ars[e];
+    return;
+  }
+  const float* __restrict__ bq = cq + (left + 1) * (M * M);
+  for (int e = t; e < M * M; e += G::TPB) {
+    qb[(e / M) * RS + e % M] = bq[e];
+    if constexpr (MOM) fb[(e / M) * RS + e % M] = cf[(left + 1) * (M * M) + e];
+  }
+  for (int e = t; e < M; e += G::TPB) rsb[e] = crs[(left + 1) * M + e];
+  __syncthreads();
+  // row a of A against B's row scales: br(a, k) = QnA(a, k) + rsB(k) - ma, ma the row's maximum
+  const int a = t / TPR, c0 = t % TPR;
+  double ma = -INFINITY;
+  for (int k = c0; k < M; k += TPR) ma = fmax(ma, (double)aq[a * M + k] + rsb[k]);
+  ma = group_max<TPR>(ma);
+  for (int k = c0; k < M; k += TPR) {
+    br[a * RS + k] = (float)(((double)aq[a * M + k] + rsb[k]) - ma);
+    if constexpr (MOM) fa[a * RS + k] = cf[left * (M * M) + a * M + k];
+  }
+  __syncthreads();
+  // columns b0 .. b0 + CPT - 1 of row a: C(a, b) = rsA(a) + ma + LSE_k (br(a, k) + QnB(k, b))
+  const int b0 = c0 * CPT;
+  float mx[CPT], sm[CPT], tm[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) { mx[u] = -INFINITY; sm[u] = 0.f; tm[u] = 0.f; }
+  for (int k = 0; k < M; ++k) {
+    const float x0 = br[a * RS + k];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) mx[u] = fmaxf(mx[u], x0 + qb[k * RS + b0 + u]);
+  }
+  for (int k = 0; k < M; ++k) {
+    const float x0 = br[a * RS + k];
+    const float f0 = MOM ? fa[a * RS + k] : 0.f;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const float e = ex2(x0 + qb[k * RS + b0 + u] - mx[u]);
+      sm[u] += e;
+      if constexpr (MOM) tm[u] = __builtin_fmaf(e, f0 + fb[k * RS + b0 + u], tm[u]);
+    }
+  }
+  float out[CPT];
+  float rmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    out[u] = mx[u] + lg2(sm[u]);
+    rmax = fmaxf(rmax, out[u]);
+  }
+  rmax = group_max<TPR>(rmax);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    oq[a * M + b0 + u] = out[u] - rmax;
+    if constexpr (MOM) pf[node * (M * M) + a * M + b0 + u] = tm[u] / sm[u];
+  }
+  if (c0 == 0) prs[node * M + a] = ars[a] + ma + (double)rmax;
+}
+
+// One wave per parent node and direction (blockIdx.y: 0 forward, 1 backward): the children's
+// boundary vectors from the parent's (zeros at the root, pv == null). Children of level 0 are
+// the segments, whose vectors are written normalised (as k_scan_wave stores them).
+struct TreeVec {
+  double* vf;  // forward vector at each node's start [chains][n][M]
+  double* vb;  // backward vector at each node's end
+  float* mf;   // Phi at the start (moments)
+  float* mb;   // Psi at the end (moments)
+};
+template <int M, bool MOM>
+__global__ void __launch_bounds__(64)
+k_tree_down(const float* __restrict__ cq, const double* __restrict__ crs,
+            const float* __restrict__ cf, long long nc, TreeVec pv, long long np, TreeVec cv,
+            double* __restrict__ lam0, double* __restrict__ rho1, double* __restrict__ sc0,
+            float* __restrict__ phi0, float* __restrict__ psi1) {
+  __shared__ float vin[M];
+  __shared__ float min_[M];
+  const long long node = blockIdx.x;
+  const long long ch = node / np, i = node % np;
+  const bool fwd = blockIdx.y == 0;
+  const int l = threadIdx.x;
+  const bool own = l < M;
+  const long long left = ch * nc + 2 * i;
+  const bool has_right = 2 * i + 1 < nc;
+  // the parent's vector
+  double v = 0.0;
+  float mom = 0.f;
+  if (pv.vf != nullptr && own) {
+    v = (fwd ? pv.vf : pv.vb)[node * M + l];
+    if constexpr (MOM) mom = (fwd ? pv.mf : pv.mb)[node * M + l];
+  }
+  auto put = [&](long long child, double x, float mo) {  // child: global index at level below
+    if (cv.vf != nullptr) {
+      if (own) {
+        (fwd ? cv.vf : cv.vb)[child * M + l] = x;
+        if constexpr (MOM) (fwd ? cv.mf : cv.mb)[child * M + l] = mo;
+      }
+    } else {
+      const double sh = floor(wave_max(own ? x : -INFINITY));
+      if (own) {
+        (fwd ? lam0 : rho1)[child * M + l] = x - sh;
+        if constexpr (MOM) (fwd ? phi0 : psi1)[child * M + l] = mo;
+      }
+      if (l == 0) sc0[child * 2 + (fwd ? 0 : 1)] = sh;
+    }
+  };
+  // the child that inherits the parent's vector: the left one going forward, the right one (or
+  // the left one without a right sibling) going backward
+  put(fwd || !has_right ? left : left + 1, v, mom);
+  if (!has_right) return;
+  // the other child: forward, start of the right child = v (x) C_left; backward, end of the left
+  // child = C_right (x) v
+  const long long m = fwd ? left : left + 1;
+  const float* __restrict__ q = cq + m * (M * M);
+  const double* __restrict__ rs = crs + m * M;
+  const float* __restrict__ f = MOM ? cf + m * (M * M) : nullptr;
+  const double rsl = own ? rs[l] : 0.0;
+  const double a_in = own ? (fwd ? v + rsl : v) : -INFINITY;
+  const double m_in = wave_max(a_in);
+  if (own) {
+    vin[l] = (float)(a_in - m_in);
+    if constexpr (MOM) min_[l] = mom;
+  }
+  __syncthreads();
+  double x = 0.0;
+  float mo = 0.f;
+  if (own) {
+    float mx = -INFINITY, sm = 0.f, tm = 0.f;
+    for (int j = 0; j < M; ++j)
+      mx = fmaxf(mx, vin[j] + (fwd ? q[j * M + l] : q[l * M + j]));
+    for (int j = 0; j < M; ++j) {
+      const int e = fwd ? j * M + l : l * M + j;
+      const float w = ex2(vin[j] + q[e] - mx);
+      sm += w;
+      if constexpr (MOM) tm = __builtin_fmaf(w, min_[j] + f[e], tm);
+    }
+    x = (fwd ? m_in : rsl + m_in) + (double)mx + (double)lg2(sm);
+    mo = MOM ? tm / sm : 0.f;
+  }
+  put(fwd ? left + 1 : left, x, mo);
+}
+
+template <int M, bool MOM>
+int run_tree(const float* rows, const double* rscale, const float* frows, int64_t chains,
+             int64_t ptot, double* lam0, double* rho1, double* sc0, float* phi0, float* psi1,
+             void* tree_ws, hipStream_t st) {
+  struct Level {
+    long long n;
+    const float* q;
+    const double* rs;
+    const float* f;
+    TreeVec v;
+  };
+  Level lv[64];
+  int top = 0;
+  lv[0] = Level{(long long)ptot, rows, rscale, frows, TreeVec{nullptr, nullptr, nullptr, nullptr}};
+  char* p = static_cast<char*>(tree_ws);
+  auto take = [&](size_t bytes) { char* r = p; p += round256(bytes); return r; };
+  for (long long n = (ptot + 1) / 2;; n = (n + 1) / 2) {
+    const size_t nodes = (size_t)chains * (size_t)n;
+    Level& L = lv[++top];
+    L.n = n;
+    float* q = reinterpret_cast<float*>(take(nodes * M * M * sizeof(float)));
+    float* f = MOM ? reinterpret_cast<float*>(take(nodes * M * M * sizeof(float))) : nullptr;
+    double* rs = reinterpret_cast<double*>(take(nodes * M * sizeof(double)));
+    L.v.vf = reinterpret_cast<double*>(take(nodes * M * sizeof(double)));
+    L.v.vb = reinterpret_cast<double*>(take(nodes * M * sizeof(double)));
+    L.v.mf = MOM ? reinterpret_cast<float*>(take(nodes * M * sizeof(float))) : nullptr;
+    L.v.mb = MOM ? reinterpret_cast<float*>(take(nodes * M * sizeof(float))) : nullptr;
+    L.q = q;
+    L.rs = rs;
+    L.f = f;
+    hipLaunchKernelGGL((k_tree_compose<M, MOM>), dim3((unsigned)nodes), dim3(TreeGeo<M>::TPB), 0,
+                       st, lv[top - 1].q, lv[top - 1].rs, lv[top - 1].f, lv[top - 1].n, q, rs, f,
+                       (long long)n);
+    if (hipGetLastError() != hipSuccess) return (int)hipErrorLaunchFailure;
+    if (n == 1) break;
+  }
+  for (int l = top; l >= 1; --l) {
+    const TreeVec pv = l == top ? TreeVec{nullptr, nullptr, nullptr, nullptr} : lv[l].v;
+    const TreeVec cv = l == 1 ? TreeVec{nullptr, nullptr, nullptr, nullptr} : lv[l - 1].v;
+    hipLaunchKernelGGL((k_tree_down<M, MOM>), dim3((unsigned)(chains * lv[l].n), 2), dim3(64), 0,
+                       st, lv[l - 1].q, lv[l - 1].rs, lv[l - 1].f, lv[l - 1].n, pv, lv[l].n, cv,
+                       lam0, rho1, sc0, phi0, psi1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
+}
+
 }  // namespace
 
 int launch_scan_bounds(const float* rows, const double* rscale, const float* frows, int64_t chains,
                        int64_t ptot, int M, double* lam0, double* rho1, double* sc0, float* phi0,
-                       float* psi1, void* stream) {
+                       float* psi1, void* tree_ws, size_t tree_ws_bytes, void* stream) {
   if (chains <= 0) return 0;
   if (M < 4 || M > 1024 || (M & (M - 1))) return (int)hipErrorInvalidValue;
   const bool mom = frows != nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // the tree where it applies (scan_tree_bytes > 0) and its workspace is given
+  const size_t need = scan_tree_bytes(chains, ptot, M, mom);
+  if (need > 0 && tree_ws != nullptr && need <= tree_ws_bytes) {
+#define BCJR_TREE(M_)                                                                           \
+  if (M == M_)                                                                                  \
+    return mom ? run_tree<M_, true>(rows, rscale, frows, chains, ptot, lam0, rho1, sc0, phi0,    \
+                                    psi1, tree_ws, st)                                          \
+               : run_tree<M_, false>(rows, rscale, frows, chains, ptot, lam0, rho1, sc0, phi0,   \
+                                     psi1, tree_ws, st);
+    BCJR_TREE(4) BCJR_TREE(8) BCJR_TREE(16) BCJR_TREE(32) BCJR_TREE(64)
+#undef BCJR_TREE
+  }
   if (M <= 64) {
 #define BCJR_WAVE(M_)                                                                           \
   if (M == M_) {                                                                                \

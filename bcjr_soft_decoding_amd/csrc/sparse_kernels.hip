@@ -1649,15 +1649,44 @@ k_sparse_bwd_wide(const float* __restrict__ cb, const float* __restrict__ w, lon
   }
 }
 
-// out[s] = sum over slots of the partials, in slot order (deterministic); with no slots, 0.
+// out[s] = sum over slots i = 0, stride, 2 stride, ... of partial[i][s], in that order
+// (deterministic); with no slots, 0.
 __global__ void __launch_bounds__(256)
 k_reduce_slots(const float* __restrict__ partial, long long slots, long long count,
-               float* __restrict__ out) {
+               long long stride, float* __restrict__ out) {
   const long long s = (long long)blockIdx.x * 256 + threadIdx.x;
   if (s >= count) return;
   float acc = 0.f;
-  for (long long i = 0; i < slots; ++i) acc += partial[(size_t)i * count + s];
+  for (long long i = 0; i < slots; i += stride) acc += partial[(size_t)i * count + s];
   out[s] = acc;
+}
+
+// Many slots are summed in two fixed-order passes instead of one chain of dependent loads per
+// state: block (x, c) adds the slots of chunk c in order and writes the sum over the chunk's
+// first row (which only that block reads), then k_reduce_slots adds the chunk sums in order.
+constexpr long long kReduceChunk = 32;
+__global__ void __launch_bounds__(256)
+k_reduce_chunks(float* __restrict__ partial, long long slots, long long count) {
+  const long long s = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (s >= count) return;
+  const long long i0 = (long long)blockIdx.y * kReduceChunk;
+  const long long i1 = i0 + kReduceChunk < slots ? i0 + kReduceChunk : slots;
+  float acc = 0.f;
+  for (long long i = i0; i < i1; ++i) acc += partial[(size_t)i * count + s];
+  partial[(size_t)i0 * count + s] = acc;
+}
+
+// out[s] = sum over the slots of partial[slot][s] (partial is scratch and may be overwritten)
+int reduce_slots(float* partial, long long slots, long long count, float* out, hipStream_t st) {
+  const unsigned gx = (unsigned)((count + 255) / 256);
+  long long stride = 1;
+  if (slots > 2 * kReduceChunk) {
+    hipLaunchKernelGGL(k_reduce_chunks, dim3(gx, (unsigned)((slots + kReduceChunk - 1) / kReduceChunk)),
+                       dim3(256), 0, st, partial, slots, count);
+    stride = kReduceChunk;
+  }
+  hipLaunchKernelGGL(k_reduce_slots, dim3(gx), dim3(256), 0, st, partial, slots, count, stride, out);
+  return (int)hipGetLastError();
 }
 
 template <int n, int k, class P>
@@ -1746,9 +1775,7 @@ int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((C::S + 255) / 256)), dim3(256), 0, st, partial,
-                     (long long)grid, (long long)C::S, grad_c);
-  return (int)hipGetLastError();
+  return reduce_slots(partial, (long long)grid, (long long)C::S, grad_c, st);
 }
 
 // Shapes whose fp32-message kernels are built in a second translation unit of this file
@@ -1969,7 +1996,7 @@ int launch_sparse_backward(const SparseGeom& g, const float* codebook, const flo
 int launch_fill_zero(float* dst, int64_t count, void* stream) {
   if (count <= 0) return 0;
   hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), nullptr, 0LL, (long long)count, dst);
+                     static_cast<hipStream_t>(stream), nullptr, 0LL, (long long)count, 1LL, dst);
   return (int)hipGetLastError();
 }
 
@@ -2016,10 +2043,8 @@ int launch_sparse_backward_seg(int mode, int n, int k, const float* codebook, co
   return (int)hipErrorInvalidValue;
 }
 
-int launch_reduce_slots(const float* partial, int64_t slots, int S, float* out, void* stream) {
-  hipLaunchKernelGGL(k_reduce_slots, dim3((unsigned)((S + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), partial, (long long)slots, (long long)S, out);
-  return (int)hipGetLastError();
+int launch_reduce_slots(float* partial, int64_t slots, int S, float* out, void* stream) {
+  return reduce_slots(partial, (long long)slots, (long long)S, out, static_cast<hipStream_t>(stream));
 }
 
 bool scan_shape_built(int n, int k) {

@@ -30,6 +30,11 @@ CASES = [
     (8, 2, 17, 1, 0.5),        # one step per segment
     (11, 2, 600, 64, 0.2),     # M = 512: several LDS tiles per transfer matrix
     (7, 3, 900, 50, 0.3),      # M = 32
+    # 64 segments and more with M <= 64: the boundary vectors come from the tree over segments
+    (4, 3, 1000, 8, 1.0),      # M = 4, 125 segments
+    (6, 2, 1300, 16, 0.3),     # M = 16, 82 segments with a ragged tail
+    (7, 2, 3000, 40, 0.2),     # M = 32, 75 segments
+    (8, 2, 5000, 64, 0.1),     # M = 64, 79 segments with a ragged tail
 ]
 
 
