@@ -35,6 +35,7 @@ CASES = [
     (6, 2, 1300, 16, 0.3),     # M = 16, 82 segments with a ragged tail
     (7, 2, 3000, 40, 0.2),     # M = 32, 75 segments
     (8, 2, 5000, 64, 0.1),     # M = 64, 79 segments with a ragged tail
+    (6, 1, 4000, 50, 0.005),   # M = 16, 80 segments at a low temperature (fp64 messages)
 ]
 
 
