@@ -249,6 +249,18 @@ __device__ __forceinline__ void chain_reduce(T (&v)[NV], double* red, int& rp) {
   }
 }
 
+// Wave priority over the per-step exchange of a chain that spans several waves (from its message
+// stores to its reduction's partial sums): the chain's waves meet at the step's barrier, so a
+// wave that issues its exchange late holds its partners; at the higher priority the SIMD
+// issues it ahead of the other chain's wave that shares it. Used in the backward, where it was
+// measured 1.7-2.4% faster at 4096 and 8192 states and within noise at 16384; the same window in
+// the forward and in the 1024-lane kernels cost 1-2% (and 13% at 8192 states, whose forward then
+// lost its second wave per SIMD to two more registers).
+template <class C, int LEVEL>
+__device__ __forceinline__ void exchange_prio() {
+  if constexpr (C::LPS > 64) __builtin_amdgcn_s_setprio(LEVEL);
+}
+
 // Vector copies between registers and memory (LDS or global), 16 bytes at a time.
 template <int N, class T>
 __device__ __forceinline__ void store_vec(T* __restrict__ dst, const T* src) {

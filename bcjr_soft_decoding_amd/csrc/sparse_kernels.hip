@@ -860,6 +860,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           mx = tmax(mx, out[g][r]);
         }
       }
+      exchange_prio<C, 1>();
       MT* mw = msgl[mb] + q * M;
       float* pw = msgp[mb] + q * M;
 #pragma unroll
@@ -869,6 +870,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       }
       MT v1[1] = {mx};
       chain_reduce<C, 1, 1u>(v1, red, rp);
+      exchange_prio<C, 0>();
       const MT sh = floor(v1[0]);
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -1081,6 +1083,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           load_hist_part<K, BLOCK>(hln, g * K, lcur[g]);
           load_hist_part<K, BLOCK>(hpn, g * K, pcur[g]);
         }
+        exchange_prio<C, 1>();
         MT* mw = msgl[mb] + q * M;
         float* pw = msgp[mb] + q * M;
         if (t > 0) {
@@ -1094,6 +1097,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         }
         MT v2[3] = {(MT)gw, mx, (MT)xs};
         chain_reduce<C, 3, 2u>(v2, red, rp);
+        exchange_prio<C, 0>();
         xbar += (float)v2[2] - h;
         {  // kept by lane t mod LPS and written once per LPS steps, as w_hat in k_sparse_fwd
           const float gwt = 2.0f * k.inv_t * ((float)v2[0] * k.csc - h * wb[t]);
