@@ -249,13 +249,13 @@ __device__ __forceinline__ void chain_reduce(T (&v)[NV], double* red, int& rp) {
   }
 }
 
-// Wave priority over the per-step exchange of a chain that spans several waves (from its message
-// stores to its reduction's partial sums): the chain's waves meet at the step's barrier, so a
-// wave that issues its exchange late holds its partners; at the higher priority the SIMD
-// issues it ahead of the other chain's wave that shares it. Used in the backward, where it was
-// measured 1.7-2.4% faster at 4096 and 8192 states and within noise at 16384; the same window in
-// the forward and in the 1024-lane kernels cost 1-2% (and 13% at 8192 states, whose forward then
-// lost its second wave per SIMD to two more registers).
+// Wave priority over the end of a step of a chain that spans several waves (its last butterfly
+// block, the message stores and the chain reduction up to its partial sums): the chain's waves
+// meet at the step's barrier, so a wave that is late holds its partners. Two waves of different
+// chains share a SIMD; raised, the one nearer its barrier issues first. Used in the backward,
+// where it was measured 5-7% faster at 4096 and 8192 states (from the message stores on, 1.7-2.4%);
+// in the forward at 8192 states the window cost two registers and the second wave per SIMD
+// (+13%), and in the 1024-lane kernels, whose waves are all of one chain, 1-2%.
 template <class C, int LEVEL>
 __device__ __forceinline__ void exchange_prio() {
   if constexpr (C::LPS > 64) __builtin_amdgcn_s_setprio(LEVEL);

@@ -838,6 +838,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       for (int g = 0; g < G; ++g) {
         float Vg[K][K];
         vsrc.get(g, Vg);
+        if (g == G - 1) exchange_prio<C, 1>();  // the step's last block and exchange
 #pragma unroll
         for (int r = 0; r < K; ++r) {
           MT x[K];
@@ -860,7 +861,6 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           mx = tmax(mx, out[g][r]);
         }
       }
-      exchange_prio<C, 1>();
       MT* mw = msgl[mb] + q * M;
       float* pw = msgp[mb] + q * M;
 #pragma unroll
@@ -1034,6 +1034,7 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int g = 0; g < G; ++g) {
           float Vg[K][K];
           vsrc.get(g, Vg);
+          if (g == G - 1) exchange_prio<C, 1>();  // the step's last block and exchange
           float fa[K], pv[K];
 #pragma unroll
           for (int a = 0; a < K; ++a) {
@@ -1083,7 +1084,6 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
           load_hist_part<K, BLOCK>(hln, g * K, lcur[g]);
           load_hist_part<K, BLOCK>(hpn, g * K, pcur[g]);
         }
-        exchange_prio<C, 1>();
         MT* mw = msgl[mb] + q * M;
         float* pw = msgp[mb] + q * M;
         if (t > 0) {
