@@ -249,13 +249,15 @@ __device__ __forceinline__ void chain_reduce(T (&v)[NV], double* red, int& rp) {
   }
 }
 
-// Wave priority over the end of a step of a chain that spans several waves (its last butterfly
-// block, the message stores and the chain reduction up to its partial sums): the chain's waves
-// meet at the step's barrier, so a wave that is late holds its partners. Two waves of different
-// chains share a SIMD; raised, the one nearer its barrier issues first. Used in the backward,
-// where it was measured 5-7% faster at 4096 and 8192 states (from the message stores on, 1.7-2.4%);
-// in the forward at 8192 states the window cost two registers and the second wave per SIMD
-// (+13%), and in the 1024-lane kernels, whose waves are all of one chain, 1-2%.
+// Wave priority by progress through a step, for chains that span several waves: the chain's
+// waves meet at the step's barrier, so a wave that is late holds its partners. Two waves of
+// different chains share a SIMD; the step's butterfly rows raise the priority a level at each
+// quarter (0 to 3), and the chain reduction lowers it to 0 once its partial sums are read, so the
+// wave nearer its barrier issues first. Used in the backward: measured 6-10% faster at 4096 and
+// 8192 states (one raised level from the last butterfly block on: 5-7%; from the message stores
+// on: 1.7-2.4%), within 1% at 16384; in the forward at 8192 states a raised window cost two
+// registers and the second wave per SIMD (+13%), and in the 1024-lane kernels, whose waves are all
+// of one chain, 1-2%.
 template <class C, int LEVEL>
 __device__ __forceinline__ void exchange_prio() {
   if constexpr (C::LPS > 64) __builtin_amdgcn_s_setprio(LEVEL);

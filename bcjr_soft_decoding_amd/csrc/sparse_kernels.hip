@@ -838,9 +838,12 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
       for (int g = 0; g < G; ++g) {
         float Vg[K][K];
         vsrc.get(g, Vg);
-        if (g == G - 1) exchange_prio<C, 1>();  // the step's last block and exchange
 #pragma unroll
         for (int r = 0; r < K; ++r) {
+          // wave priority up a level at each quarter of the step (lowered after the reduction)
+          if (g * K + r == G * K / 4) exchange_prio<C, 1>();
+          if (g * K + r == G * K / 2) exchange_prio<C, 2>();
+          if (g * K + r == 3 * G * K / 4) exchange_prio<C, 3>();
           MT x[K];
           MT m = (MT)-INFINITY;
 #pragma unroll
@@ -1034,10 +1037,13 @@ k_sparse_bwd(const float* __restrict__ cb, const float* __restrict__ w, long lon
         for (int g = 0; g < G; ++g) {
           float Vg[K][K];
           vsrc.get(g, Vg);
-          if (g == G - 1) exchange_prio<C, 1>();  // the step's last block and exchange
           float fa[K], pv[K];
 #pragma unroll
           for (int a = 0; a < K; ++a) {
+            // wave priority up a level at each quarter of the step (as in advance)
+            if (g * K + a == G * K / 4) exchange_prio<C, 1>();
+            if (g * K + a == G * K / 2) exchange_prio<C, 2>();
+            if (g * K + a == 3 * G * K / 4) exchange_prio<C, 3>();
             MT y[K];
             float dd[K];
             MT m = (MT)-INFINITY;
