@@ -136,9 +136,18 @@ __device__ __forceinline__ void product(const float* __restrict__ xs, const floa
   f4 acc[2][2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) acc[s][0] = acc[s][1] = f4{0.f, 0.f, 0.f, 0.f};
+  // The message operands are read from LDS PD chunks (8 MFMAs each) ahead of their matrix
+  // instructions; the scheduling barrier keeps each read in its chunk (left to itself the
+  // scheduler sinks every read to one chunk ahead, and each chunk then waits for its read).
+  constexpr int PD = 3, NCH = C::KC / 4;
+  f4 pre[NCH];
+#pragma unroll
+  for (int i = 0; i < PD && i < NCH; ++i) pre[i] = *reinterpret_cast<const f4*>(xr + 4 * i);
 #pragma unroll
   for (int kc = 0; kc < C::KC; kc += 4) {
-    const f4 a = *reinterpret_cast<const f4*>(xr + kc);
+    if (kc / 4 + PD < NCH) pre[kc / 4 + PD] = *reinterpret_cast<const f4*>(xr + kc + 4 * PD);
+    __builtin_amdgcn_sched_barrier(0);
+    const f4 a = pre[kc / 4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[0][e & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], m[2 * (kc + e)], acc[0][e & 1], 0, 0, 0);
