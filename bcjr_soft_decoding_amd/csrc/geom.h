@@ -47,6 +47,21 @@ constexpr int geom_spb(int n, int k, int kind) {
 constexpr int geom_block(int n, int k, int kind) {
   return geom_lps(n, k, kind) < 64 ? 64 : geom_lps(n, k, kind);
 }
+// Batches too small to fill the device in the target geometry: the fp32-message forward and
+// backward of whole chains then take the segment kinds' geometry (16 states per lane: 4x the
+// forward's lanes per chain, 2x the backward's), which spreads each step's work over more
+// waves. Chosen from (n, k, B) alone, so that the workspace query and the launch agree; built
+// where the segment kernels are (k = 2, n <= 12) and only where it adds lanes. Thresholds, in
+// waves of the target geometry on the 1024 SIMDs, measured on MI355X (L = 256, n = 6..12):
+// below them the spread geometry was up to 2.6x faster, above them up to 13% slower.
+constexpr long long kSpreadFwdBelowWaves = 2048, kSpreadBwdBelowWaves = 1024;
+constexpr bool geom_spread(int n, int k, long long B, int kind) {
+  return (kind == kFwd || kind == kBwd) && k == 2 && n <= 12 &&
+         geom_g(n, k, kind == kFwd ? kFwdS : kBwdS) < geom_g(n, k, kind) &&
+         (B + geom_spb(n, k, kind) - 1) / geom_spb(n, k, kind) * (geom_block(n, k, kind) / 64) <
+             (kind == kFwd ? kSpreadFwdBelowWaves : kSpreadBwdBelowWaves);
+}
+
 // Below this temperature the forward-backward carries its messages in fp64 (their fp32
 // rounding, which grows like 1/T, would put the gradient outside 1e-3). The fp64-message
 // backward needs both of a chain's message buffers (fp64 + fp32 per butterfly, single-buffered)
@@ -72,5 +87,8 @@ static_assert(geom_g(4, 2, kFwd) == 1 && geom_lps(4, 2, kFwd) == 1, "S=16 geomet
 static_assert(geom_g(8, 2, kBwd) == 2 && geom_lps(8, 2, kBwd) == 8, "S=256 geometry");
 static_assert(geom_g(8, 2, kFwdS) == 1 && geom_lps(8, 2, kBwdS) == 16, "S=256 segment geometry");
 static_assert(geom_precise_fits(15, 2) && !geom_precise_fits(16, 2), "fp64 messages up to S=2^15");
+static_assert(geom_spread(8, 2, 4096, kFwd) && geom_spread(8, 2, 4096, kBwd) &&
+              !geom_spread(12, 2, 65536, kFwd) && !geom_spread(12, 2, 65536, kBwd) &&
+              !geom_spread(4, 2, 16, kFwd) && !geom_spread(16, 2, 1, kBwd), "spread geometry rule");
 
 }  // namespace bcjr

@@ -51,10 +51,16 @@ size_t bwd_ws_one(const SparseGeom& g, int64_t L, bool ckpt) {
 }
 }  // namespace
 
+// The forward and backward workspaces hold the largest of the layouts the launch may take:
+// the target geometry (or, for small batches, the spread one) and the fp64-message one.
 size_t sparse_fwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
   size_t need = fwd_ws_one(g, L, ckpt);
   SparseGeom p;
   if (sparse_geom(g.n, g.k, g.B, kFwdP, &p)) {
+    const size_t q = fwd_ws_one(p, L, ckpt);
+    if (q > need) need = q;
+  }
+  if (geom_spread(g.n, g.k, g.B, kFwd) && sparse_geom(g.n, g.k, g.B, kFwdS, &p)) {
     const size_t q = fwd_ws_one(p, L, ckpt);
     if (q > need) need = q;
   }
@@ -64,6 +70,10 @@ size_t sparse_bwd_ws_bytes(const SparseGeom& g, int64_t L, bool ckpt) {
   size_t need = bwd_ws_one(g, L, ckpt);
   SparseGeom p;
   if (sparse_geom(g.n, g.k, g.B, kBwdP, &p)) {
+    const size_t q = bwd_ws_one(p, L, ckpt);
+    if (q > need) need = q;
+  }
+  if (geom_spread(g.n, g.k, g.B, kBwd) && sparse_geom(g.n, g.k, g.B, kBwdS, &p)) {
     const size_t q = bwd_ws_one(p, L, ckpt);
     if (q > need) need = q;
   }

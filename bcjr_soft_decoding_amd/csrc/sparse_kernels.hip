@@ -1699,11 +1699,11 @@ int reduce_slots(float* partial, long long slots, long long count, float* out, h
   return (int)hipGetLastError();
 }
 
-template <int n, int k, class P>
+template <int n, int k, class P, int KIND = fwd_kind<P>()>
 int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, float* w_hat, float* log_z, float* saved, void* ws, bool ckpt,
               hipStream_t st) {
-  using C = Cfg<(1 << k), geom_g(n, k, fwd_kind<P>()), geom_lps(n, k, fwd_kind<P>()), P, false>;
+  using C = Cfg<(1 << k), geom_g(n, k, KIND), geom_lps(n, k, KIND), P, false>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
   const Consts kc = make_consts(T, P::kExactEmit);
@@ -1742,11 +1742,11 @@ int run_fwd_p(const SparseGeom& g, const float* cb, const float* w, long long B,
   }
 }
 
-template <int n, int k, class P>
+template <int n, int k, class P, int KIND = bwd_kind<P>()>
 int run_bwd_p(const SparseGeom& g, const float* cb, const float* w, long long B, long long L,
               float T, const float* saved, const float* gup, const float* hup, float* grad_w,
               float* grad_c, void* ws, bool ckpt, hipStream_t st) {
-  using C = Cfg<(1 << k), geom_g(n, k, bwd_kind<P>()), geom_lps(n, k, bwd_kind<P>()), P, true>;
+  using C = Cfg<(1 << k), geom_g(n, k, KIND), geom_lps(n, k, KIND), P, true>;
   static_assert(C::S == (1 << n), "geometry mismatch");
   if (g.G != C::G || g.LPS != C::LPS) return (int)hipErrorInvalidValue;
   const Consts kc = make_consts(T, P::kExactEmit);
@@ -1815,6 +1815,13 @@ int run_fwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
     if (T < kPreciseBelowT)
       return run_fwd_p<n, k, Mixed>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
   }
+  if constexpr (k == 2 && n <= 12) {
+    if (geom_spread(n, k, B, kFwd)) {  // a batch too small for the target geometry
+      SparseGeom gs;
+      if (!sparse_geom(n, k, B, kFwdS, &gs)) return (int)hipErrorInvalidValue;
+      return run_fwd_p<n, k, Fast, kFwdS>(gs, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+    }
+  }
   if constexpr (ilp_fwd_shape(n, k))
     return run_fwd_fast_ilp(n, g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
   else
@@ -1836,6 +1843,14 @@ int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
     if (T < kPreciseBelowT)
       return run_bwd_p<n, k, Mixed>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt,
                                     st);
+  }
+  if constexpr (k == 2 && n <= 12) {
+    if (geom_spread(n, k, B, kBwd)) {  // a batch too small for the target geometry
+      SparseGeom gs;
+      if (!sparse_geom(n, k, B, kBwdS, &gs)) return (int)hipErrorInvalidValue;
+      return run_bwd_p<n, k, Fast, kBwdS>(gs, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws,
+                                          ckpt, st);
+    }
   }
   if constexpr (ilp_bwd_shape(n, k))
     return run_bwd_fast_ilp(n, g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt, st);

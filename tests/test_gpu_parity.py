@@ -113,7 +113,8 @@ def test_edge_shapes(n, B, L):
 
 # The per-step outputs (w_hat, grad_w) are kept by lane t mod LPS of a chain and written once
 # per LPS steps: lengths with several windows and a partial first one, at the geometries of
-# one-wave (LPS 64 forward), two-wave (LPS 128 backward) and four-wave (LPS 256) chains.
+# one-wave (LPS 64), two-wave (LPS 128) and four-wave (LPS 256) chains (these small batches take
+# the spread geometry at n <= 12, the target one at n = 13).
 @pytest.mark.parametrize("n,B,L", [(12, 3, 129), (12, 2, 257), (13, 2, 300), (11, 4, 95),
                                    (10, 5, 65)])
 def test_output_windows(n, B, L):
@@ -121,6 +122,72 @@ def test_output_windows(n, B, L):
     w = synth.normal(820 + n + L, (B, L))
     g = synth.normal(920 + n + L, (B, L))
     _compare(n, 2, c, w, 0.15, g, None, "windows")
+
+
+# Geometry by batch size: below a wave count of the target geometry (2048 waves forward, 1024
+# backward) the fp32-message kernels at n <= 12 spread each chain over 4x / 2x the lanes. The
+# small batches of the other tests take the spread geometry; these batches are the smallest that
+# take the target geometry in both kernels (short chains keep the oracle cheap), plus batches where
+# only the forward spreads, and ragged batches on either side of the thresholds.
+def _target_geometry_batch(n):
+    """Smallest B for which both the forward and the backward keep the target geometry."""
+    ng = 1 << (n - 4)
+    def waves(states_per_lane_log2):
+        g = max(min(max((1 << states_per_lane_log2) >> 4, 1), ng), 1)
+        lps = ng // g
+        spb = 64 // lps if lps < 64 else 1
+        block = 64 if lps < 64 else lps
+        return spb, block // 64
+    fs, fw = waves(6)   # forward: 64 states per lane
+    bs, bw = waves(5)   # backward: 32 states per lane
+    return max(2048 // fw * fs, 1024 // bw * bs)
+
+
+@pytest.mark.parametrize("n", list(range(5, 13)))
+def test_target_geometry_large_batch(n):
+    B = _target_geometry_batch(n) + 3  # ragged: the last unit is partly empty
+    L = max(2, min(6, (40_000_000 // (B << n))))
+    c = synth.normal(740 + n, (1 << n,))
+    w = synth.normal(840 + n, (B, L))
+    g = synth.normal(940 + n, (B, L))
+    h = synth.normal(1040 + n, (B,))
+    log_case(f"target-geometry n={n} B={B} L={L}")
+    got = run_fwd_bwd(n, 2, c, w, 0.2, g, h)
+    ref = oracle.sparse_forward(n, 2, c, w, 0.2)
+    rb = oracle.sparse_backward(n, 2, c, w, 0.2, g, h)
+    _check_short(got, ref, rb)
+
+
+def _check_short(got, ref, rb):
+    """Short chains: log Z compared normwise over the batch (reading R20: some chain's log Z may
+    lie near zero), every other output as in _compare."""
+    assert_normwise(got["w_hat"], ref["w_hat"], RTOL_FWD, "w_hat")
+    assert_normwise(got["log_z"], ref["log_z"], RTOL_FWD, "log_z")
+    assert_normwise(got["grad_w"], rb["grad_w"], RTOL_GRAD, "grad_w")
+    assert_normwise(got["grad_codebook"], rb["grad_codebook"], RTOL_GRAD, "grad_codebook")
+
+
+@pytest.mark.parametrize("n,B,L,ckpt", [(8, 8200, 24, False), (12, 1500, 20, False),
+                                        (10, 2045, 17, True), (12, 511, 40, True),
+                                        (8, 4095, 9, True)])
+def test_spread_geometry_boundaries(n, B, L, ckpt):
+    """(8, 8200) and (12, 1500): the forward spreads, the backward keeps the target geometry;
+    the others spread both, with the checkpointed history where ckpt is set."""
+    c = synth.normal(760 + n, (1 << n,))
+    w = synth.normal(860 + n + L, (B, L))
+    g = synth.normal(960 + n + L, (B, L))
+    log_case(f"spread n={n} B={B} L={L} ckpt={ckpt}")
+    cd, wd = dev(c), dev(w)
+    wf = bcjr.workspace(n, 2, B, L, bcjr.FWD_CKPT if ckpt else bcjr.FWD)
+    wb = bcjr.workspace(n, 2, B, L, bcjr.BWD_CKPT if ckpt else bcjr.BWD)
+    w_hat, log_z, saved = bcjr.bcjr_forward(cd, wd, n, 2, 0.1, ws=wf)
+    gw, gc = bcjr.bcjr_backward(cd, wd, n, 2, 0.1, saved, dev(g), ws=wb)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_forward(n, 2, c, w, 0.1)
+    rb = oracle.sparse_backward(n, 2, c, w, 0.1, g)
+    got = {"w_hat": w_hat.cpu().numpy(), "log_z": log_z.cpu().numpy(), "grad_w": gw.cpu().numpy(),
+           "grad_codebook": gc.cpu().numpy()}
+    _check_short(got, ref, rb)
 
 
 def test_zero_chains_is_a_no_op():
