@@ -53,7 +53,7 @@ constexpr int geom_block(int n, int k, int kind) {
 // waves. Chosen from (n, k, B) alone, so that the workspace query and the launch agree; built
 // where the segment kernels are (k = 2, n <= 12) and only where it adds lanes. Thresholds, in
 // waves of the target geometry on the 1024 SIMDs, measured on MI355X (L = 256, n = 6..12):
-// below them the spread geometry was up to 2.6x faster, above them up to 13% slower.
+// below them the spread geometry was up to 2.5x faster, above them up to 19% slower.
 constexpr long long kSpreadFwdBelowWaves = 2048, kSpreadBwdBelowWaves = 1024;
 constexpr bool geom_spread(int n, int k, long long B, int kind) {
   return (kind == kFwd || kind == kBwd) && k == 2 && n <= 12 &&

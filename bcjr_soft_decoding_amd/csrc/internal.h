@@ -100,6 +100,14 @@ int run_fwd_fast_ilp(int n, const SparseGeom& g, const float* cb, const float* w
 int run_bwd_fast_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
                      long long L, float T, const float* saved, const float* gup, const float* hup,
                      float* grad_w, float* grad_c, void* ws, bool ckpt, void* stream);
+// The same in the spread geometry of small batches (k = 2, n <= 12; see geom_spread).
+int run_fwd_spread_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
+                       long long L, float T, float* w_hat, float* log_z, float* saved, void* ws,
+                       bool ckpt, void* stream);
+int run_bwd_spread_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
+                       long long L, float T, const float* saved, const float* gup,
+                       const float* hup, float* grad_w, float* grad_c, void* ws, bool ckpt,
+                       void* stream);
 int launch_fill_zero(float* dst, int64_t count, void* stream);
 // Grid of a persistent kernel: min(slots, resident blocks on the current device), or -1.
 int resident_grid(const void* kernel, int block, int64_t slots);

@@ -1797,6 +1797,8 @@ constexpr bool ilp_fwd_shape(int n, int k) {
   return k == 2 && (n == 12 || n == 13 || n == 15 || n == 16);
 }
 constexpr bool ilp_bwd_shape(int n, int k) { return k == 2 && n >= 9 && n <= 14; }
+// The spread-geometry kernels of small batches (one wave or less per SIMD, so bound by each
+// step's latency) are built there too: forward 2-5% faster at n = 8, 10, 12, backward within 1%.
 // The segmented backward's transfer and moment rows (BM 2): 4.5-8.4% faster at n = 8, 10, 12
 // with that schedule (neutral at n = 4; its segment launches, BM 1, are neutral too).
 constexpr bool ilp_bwd_seg_shape(int n, int k, int BM) { return k == 2 && n <= 12 && BM == 2; }
@@ -1819,7 +1821,7 @@ int run_fwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
     if (geom_spread(n, k, B, kFwd)) {  // a batch too small for the target geometry
       SparseGeom gs;
       if (!sparse_geom(n, k, B, kFwdS, &gs)) return (int)hipErrorInvalidValue;
-      return run_fwd_p<n, k, Fast, kFwdS>(gs, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+      return run_fwd_spread_ilp(n, gs, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
     }
   }
   if constexpr (ilp_fwd_shape(n, k))
@@ -1848,8 +1850,8 @@ int run_bwd(const SparseGeom& g, const float* cb, const float* w, long long B, l
     if (geom_spread(n, k, B, kBwd)) {  // a batch too small for the target geometry
       SparseGeom gs;
       if (!sparse_geom(n, k, B, kBwdS, &gs)) return (int)hipErrorInvalidValue;
-      return run_bwd_p<n, k, Fast, kBwdS>(gs, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws,
-                                          ckpt, st);
+      return run_bwd_spread_ilp(n, gs, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt,
+                                st);
     }
   }
   if constexpr (ilp_bwd_shape(n, k))
@@ -1955,6 +1957,31 @@ int run_bwd_fast_ilp(int n, const SparseGeom& g, const float* cb, const float* w
     if (n == N_)                 \
       return run_bwd_p<N_, 2, Fast>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, ckpt, st);
   X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+#undef X
+  return (int)hipErrorInvalidValue;
+}
+
+int run_fwd_spread_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
+                       long long L, float T, float* w_hat, float* log_z, float* saved, void* ws,
+                       bool ckpt, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define X(N_) \
+  if (n == N_) return run_fwd_p<N_, 2, Fast, kFwdS>(g, cb, w, B, L, T, w_hat, log_z, saved, ws, ckpt, st);
+  X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12)
+#undef X
+  return (int)hipErrorInvalidValue;
+}
+
+int run_bwd_spread_ilp(int n, const SparseGeom& g, const float* cb, const float* w, long long B,
+                       long long L, float T, const float* saved, const float* gup,
+                       const float* hup, float* grad_w, float* grad_c, void* ws, bool ckpt,
+                       void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define X(N_)                                                                                 \
+  if (n == N_)                                                                                \
+    return run_bwd_p<N_, 2, Fast, kBwdS>(g, cb, w, B, L, T, saved, gup, hup, grad_w, grad_c, ws, \
+                                         ckpt, st);
+  X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12)
 #undef X
   return (int)hipErrorInvalidValue;
 }
