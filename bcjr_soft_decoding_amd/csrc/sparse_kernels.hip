@@ -26,10 +26,10 @@
 // Precision policies. The messages lam and rho are sums along the trellis of emission terms
 // whose size grows like 1/T. In fp32 their accumulated rounding (about an ulp of a value of
 // size log2(e)/T per step) limits the gradient, whose sensitivity to posterior errors is
-// large when T is small, so below T = 0.01 the messages are carried in fp64 and the emission
+// large when T is small, so below T = 0.05 (kPreciseBelowT) the messages are carried in fp64 and the emission
 // is formed from the unscaled difference w - c; exponentials, the posterior weights and the
 // conditional expectations stay fp32 in both policies. The 2^16-state trellis keeps fp32
-// messages at every T (its fp64 backward messages would not fit in LDS) and below T = 0.01 forms
+// messages at every T (its fp64 backward messages would not fit in LDS) and below T = 0.05 forms
 // only the emission in fp64 (the Mixed policy).
 //
 // One persistent block per workspace slot loops over chain units. Phase A runs the forward

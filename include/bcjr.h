@@ -103,10 +103,11 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
  * ws     DEVICE, ws_bytes >= bcjr_workspace_bytes(tr, B, L, 3) (checkpointed history) or
  *        >= bcjr_workspace_bytes(tr, B, L, 0) (full history); contents are scratch
  * B = 0 is valid and enqueues nothing. B * L may not exceed 2^40 (BCJR_E_SHAPE).
- * Temperature and precision: below T = 0.01 the messages are carried in fp64 (their fp32
- * rounding grows like 1/T and would put the gradient outside 1e-3), above in fp32. The fp64
+ * Temperature and precision: below T = 0.05 the messages are carried in fp64 (their fp32
+ * rounding grows like 1/T; at unit-scale inputs it put rare chains' gradients at 0.8-1.2e-3 for
+ * T in [0.012, 0.03] and within 3.1e-4 from T = 0.04 on), from T = 0.05 on in fp32. The fp64
  * kernels exist for every state size whose backward message buffers fit the 160 KiB of LDS,
- * i.e. n <= 15 at k = 2. For n = 16 (S = 2^16) the messages stay fp32 and below T = 0.01 only
+ * i.e. n <= 15 at k = 2. For n = 16 (S = 2^16) the messages stay fp32 and below T = 0.05 only
  * the emission -(w - c)^2 / T and its sum with the message are formed in fp64 (w - c exactly),
  * which keeps the tolerances down to T = 0.004 for w and c of unit scale (inputs of scale lam
  * behave like unit-scale ones at T / lam^2); below T = 0.004 bcjr_forward and bcjr_backward

@@ -104,7 +104,7 @@ def test_forward_rejects_bad_arguments_without_device(lib):
 
 
 def test_temperatures_below_the_fp64_threshold_need_fp64_kernels(lib):
-    """Below T = 0.01 the messages are fp64; the 2^16-state trellis has no such kernels (its
+    """Below T = 0.05 the messages are fp64; the 2^16-state trellis has no such kernels (its
     message buffers would not fit LDS), keeps fp32 messages with an fp64 emission down to
     T = 0.004 and is refused below, before any device call."""
     for T in (0.0039, 0.002, 1e-4):

@@ -103,9 +103,9 @@ def test_2_16_states_below_0004_refused(T):
 
 
 @pytest.mark.parametrize("seed,B,L", [(7500, 5, 24), (7600, 6, 40)])
-@pytest.mark.parametrize("T", [0.0099, 0.006, 0.004])
-def test_2_16_states_below_001_fp64_emission(T, seed, B, L):
-    """Below T = 0.01 the 2^16-state kernels keep fp32 messages and form the emission in fp64
+@pytest.mark.parametrize("T", [0.02, 0.0099, 0.006, 0.004])
+def test_2_16_states_below_threshold_fp64_emission(T, seed, B, L):
+    """Below T = 0.05 the 2^16-state kernels keep fp32 messages and form the emission in fp64
     (w - c exactly, its square and its sum with the message in fp64). Against the oracle, both
     histories, on the input whose gradient erred by 0.51 at T = 0.002 with the fp32 emission
     (a near-tie between paths; seed 7500) and on a second one."""
@@ -126,9 +126,15 @@ def test_2_16_states_below_001_fp64_emission(T, seed, B, L):
 
 
 def test_2_16_states_at_the_threshold_match_oracle():
-    """T = 0.01 exactly, the lowest temperature of the fp32 emission at 2^16 states, against the
-    oracle on the input that erred by 0.51 at T = 0.002 with the fp32 emission."""
-    n, B, L, T = 16, 5, 24, 0.01
+    """T = 0.05 exactly, the lowest temperature of the fp32 emission at 2^16 states, and T = 0.01
+    (the fp64 emission), against the oracle on the input that erred by 0.51 at T = 0.002 with the
+    fp32 emission."""
+    for T in (0.05, 0.01):
+        _threshold_case(T)
+
+
+def _threshold_case(T):
+    n, B, L = 16, 5, 24
     c = synth.normal(7500, (1 << n,))
     w = synth.normal(7501, (B, L))
     g = synth.normal(7502, (B, L))
@@ -136,7 +142,7 @@ def test_2_16_states_at_the_threshold_match_oracle():
     ref = oracle.sparse_forward(n, 2, c, w, T)
     rb = oracle.sparse_backward(n, 2, c, w, T, g, h)
     for hist in ("full", "ckpt"):
-        log_case(f"n=16 T=0.01 history={hist}")
+        log_case(f"n=16 T={T} history={hist}")
         got = _run(n, c, w, g, h, T, hist == "ckpt")
         assert_normwise(got["w_hat"], ref["w_hat"], RTOL_FWD, f"{hist} w_hat")
         assert_rel(got["log_z"], ref["log_z"], RTOL_FWD, f"{hist} log_z")

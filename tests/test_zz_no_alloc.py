@@ -63,7 +63,7 @@ def test_two_calls_in_a_row_second_smaller():
 
 
 def test_fp64_messages_and_ragged_chains():
-    # below T = 0.01 the forward carries fp64 messages; an odd chain count leaves a ragged unit
+    # below T = 0.05 the forward carries fp64 messages; an odd chain count leaves a ragged unit
     assert _compare(8, 29, 65, 0.005, seed=13) == "full"
     assert _compare(10, 3, 7, 0.05, seed=14) == "full"
 
