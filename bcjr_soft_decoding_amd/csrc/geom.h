@@ -74,6 +74,11 @@ constexpr bool geom_spread(int n, int k, long long B, int kind) {
 // and c of unit scale); the entry points refuse lower temperatures for those shapes.
 constexpr float kPreciseBelowT = 0.05f;
 constexpr float kMixedFloorT = 0.004f;
+// The fp64-message kernels keep exponentials, posteriors and expectations in fp32, whose rounding
+// the gradient amplifies like 1/T: at unit-scale inputs (n = 5..12, L up to 256) their worst
+// grad_w was 7.8e-5 at T = 0.004, 1.5e-4 at 0.002, 4.9e-4 at 0.001 and 2.1e-3 at 0.0005, so the
+// entry points refuse temperatures below this floor (the Viterbi decoder is the T -> 0 limit).
+constexpr float kPreciseFloorT = 0.002f;
 constexpr bool geom_precise_fits(int n, int k) {
   return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;
 }

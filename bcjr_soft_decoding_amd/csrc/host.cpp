@@ -115,8 +115,10 @@ bool temp_ok(float T) { return isfinite(T) && T > 0.0f; }
 // Shapes without fp64-message kernels (geom_precise_fits false) keep fp32 messages, with the
 // emission formed in fp64 below kPreciseBelowT; their gradient leaves 1e-3 below kMixedFloorT:
 // refused there.
+// Shapes with fp64-message kernels meet them down to kPreciseFloorT and are refused below it.
 bool temp_supported(const bcjr_trellis* tr, float T) {
-  return T >= kMixedFloorT || geom_precise_fits(tr->state_bits, tr->bits_per_step);
+  return geom_precise_fits(tr->state_bits, tr->bits_per_step) ? T >= kPreciseFloorT
+                                                               : T >= kMixedFloorT;
 }
 
 // Workspaces are accessed with 16-byte vector loads and stores.
@@ -211,6 +213,7 @@ bcjr_status bcjr_backward_scan(const bcjr_trellis* tr, const float* w, int64_t B
   bcjr_status st = scan_setup_bwd(tr, B, L, seg_len, &plan);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
+  if (!temp_supported(tr, T)) return BCJR_E_UNSUPPORTED;
   if (grad_codebook == nullptr || tr->codebook == nullptr) return BCJR_E_ARG;
   if (B == 0)
     return from_hip(launch_fill_zero(grad_codebook, (int64_t)1 << tr->state_bits, stream));
@@ -291,6 +294,7 @@ bcjr_status bcjr_forward_scan(const bcjr_trellis* tr, const float* w, int64_t B,
   bcjr_status st = scan_setup(tr, B, L, seg_len, &plan);
   if (st != BCJR_OK) return st;
   if (!temp_ok(T)) return BCJR_E_ARG;
+  if (!temp_supported(tr, T)) return BCJR_E_UNSUPPORTED;
   if (B == 0) return BCJR_OK;
   if (!w || !w_hat || !log_z || tr->codebook == nullptr) return BCJR_E_ARG;
   if (!ws_ok(ws, ws_bytes, plan.bytes)) return BCJR_E_WORKSPACE;

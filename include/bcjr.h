@@ -111,7 +111,11 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
  * the emission -(w - c)^2 / T and its sum with the message are formed in fp64 (w - c exactly),
  * which keeps the tolerances down to T = 0.004 for w and c of unit scale (inputs of scale lam
  * behave like unit-scale ones at T / lam^2); below T = 0.004 bcjr_forward and bcjr_backward
- * return BCJR_E_UNSUPPORTED for n = 16, before enqueueing anything.
+ * return BCJR_E_UNSUPPORTED for n = 16, before enqueueing anything. The fp64-message kernels
+ * (n <= 15) meet the tolerances down to T = 0.002 (their exponentials and expectations are fp32;
+ * at unit-scale inputs rare gradients reached 2e-3 at T = 0.0005): below T = 0.002 the soft
+ * entry points (bcjr_forward, bcjr_backward, bcjr_forward_scan, bcjr_backward_scan) return
+ * BCJR_E_UNSUPPORTED for every state size; viterbi_decode is the T -> 0 limit.
  */
 bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                          float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,

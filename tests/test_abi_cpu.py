@@ -120,7 +120,31 @@ def test_temperatures_below_the_fp64_threshold_need_fp64_kernels(lib):
     for T in (0.004, 0.006, 0.01):
         assert _fwd(lib, n=16, T=T, wsb=0) == bcjr.BCJR_E_WORKSPACE
     for n in range(4, 16):
-        assert _fwd(lib, n=n, T=0.001, wsb=0) == bcjr.BCJR_E_WORKSPACE
+        assert _fwd(lib, n=n, T=0.002, wsb=0) == bcjr.BCJR_E_WORKSPACE
+
+
+def test_temperatures_below_the_fp64_floor_are_refused(lib):
+    """The fp64-message kernels meet the tolerances down to T = 0.002 (their fp32 exponentials and
+    expectations put rare gradients at 2e-3 by T = 0.0005); below it every soft entry point of the
+    bitshift trellis, whole-chain and segmented, refuses before any device call."""
+    P = ctypes.c_void_p
+    for n in (4, 8, 12, 15):
+        for T in (0.0019, 0.001, 1e-5):
+            assert _fwd(lib, n=n, T=T) == bcjr.BCJR_E_UNSUPPORTED
+            assert _fwd(lib, n=n, T=T, B=0, w=0, wh=0, lz=0, sv=0, ws=0, wsb=0) == bcjr.BCJR_E_UNSUPPORTED
+            tr = bcjr.Trellis(n, 2, 1, 0x1000)
+            st = lib.bcjr_backward(ctypes.byref(tr), P(0x2000), 4, 8, T, P(0x3000), P(0x4000), None,
+                                   P(0x5000), P(0x6000), P(0x7000), 1 << 40, None)
+            assert st == bcjr.BCJR_E_UNSUPPORTED
+        if n <= 12:
+            tr = bcjr.Trellis(n, 2, 1, 0x1000)
+            for T, want in ((0.001, bcjr.BCJR_E_UNSUPPORTED), (0.002, bcjr.BCJR_E_WORKSPACE)):
+                st = lib.bcjr_forward_scan(ctypes.byref(tr), P(0x2000), 1, 4096, T, 0, P(0x3000),
+                                           P(0x4000), P(0x5000), 0, None)
+                assert st == want, (n, T, st)
+                st = lib.bcjr_backward_scan(ctypes.byref(tr), P(0x2000), 1, 4096, T, 0, P(0x3000),
+                                            P(0x4000), None, P(0x5000), P(0x6000), P(0x7000), 0, None)
+                assert st == want, (n, T, st)
 
 
 def test_backward_and_viterbi_reject_bad_arguments_without_device(lib):

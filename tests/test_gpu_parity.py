@@ -5,8 +5,8 @@ import torch
 
 import oracle
 from bcjr_soft_decoding_amd import bcjr, synth
-from tests.gpu_helpers import (RTOL_FWD, RTOL_GRAD, assert_normwise, assert_rel, dev, log_case,
-                               run_fwd_bwd)
+from tests.gpu_helpers import (RTOL_FWD, RTOL_GRAD, assert_normwise, assert_refused, assert_rel, dev,
+                               log_case, run_fwd_bwd)
 
 pytestmark = pytest.mark.gpu
 
@@ -217,6 +217,19 @@ def test_fp32_envelope_cases_take_fp64_messages(n, B, L, T, ckpt, seed):
     _check_short(got, ref, rb)
     # margin: the fp64 path holds these well inside the bar (the fp32 one reached 0.8-1.2e-3)
     assert_normwise(got["grad_w"], rb["grad_w"], RTOL_GRAD / 4, "grad_w (margin)")
+
+
+# Below T = 0.002 the fp64-message kernels' fp32 exponentials and expectations put rare gradients
+# outside 1e-3 (these two inputs: 2.1e-3 and 1.7e-3 at T = 0.0005): refused there, before any launch.
+@pytest.mark.parametrize("n,B,L,seed", [(9, 7, 64, 543067593), (12, 23, 256, 679462638)])
+@pytest.mark.parametrize("T", [0.0005, 0.0019])
+def test_below_the_fp64_floor_is_refused(n, B, L, seed, T):
+    r = np.random.default_rng(seed)
+    c = r.standard_normal(1 << n, dtype=np.float32)
+    w = r.standard_normal((B, L), dtype=np.float32)
+    g = r.standard_normal((B, L), dtype=np.float32)
+    log_case(f"floor refusal n={n} B={B} L={L} T={T}")
+    assert_refused(n, 2, c, w, T, g)
 
 
 def test_zero_chains_is_a_no_op():
