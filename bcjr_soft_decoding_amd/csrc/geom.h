@@ -70,15 +70,19 @@ constexpr bool geom_spread(int n, int k, long long B, int kind) {
 // messages at most 6.4e-5 below the threshold). The fp64-message
 // backward needs both of a chain's message buffers (fp64 + fp32 per butterfly, single-buffered)
 // in LDS; shapes where they do not fit (S = 2^16 at k = 2) keep fp32 messages and form only the
-// emission in fp64 below the threshold, which meets the tolerances down to kMixedFloorT (at w
-// and c of unit scale); the entry points refuse lower temperatures for those shapes.
+// emission in fp64 below the threshold.
 constexpr float kPreciseBelowT = 0.05f;
-constexpr float kMixedFloorT = 0.004f;
-// The fp64-message kernels keep exponentials, posteriors and expectations in fp32, whose rounding
-// the gradient amplifies like 1/T: at unit-scale inputs (n = 5..12, L up to 256) their worst
-// grad_w was 7.8e-5 at T = 0.004, 1.5e-4 at 0.002, 4.9e-4 at 0.001 and 2.1e-3 at 0.0005, so the
-// entry points refuse temperatures below this floor (the Viterbi decoder is the T -> 0 limit).
-constexpr float kPreciseFloorT = 0.002f;
+// Lowest temperature each state size meets the tolerances at; the soft entry points refuse lower
+// ones (the Viterbi decoder is the T -> 0 limit). Exponentials, posteriors and expectations are
+// fp32 on every path, and near-ties between paths amplify their rounding in the gradient like 1/T,
+// more often the more states there are. Randomized sweeps at unit-scale inputs (L up to 256),
+// worst grad_w: n <= 12 (fp64 messages) 1.7e-4 at T = 0.002..0.003, 2.1e-3 at 0.0005;
+// n = 13..15 (fp64 messages) 1.0e-3 at 0.01, 7.2e-3 and 0.24 at 0.002, within 9.6e-5 over 76
+// cases at 0.012; n = 16 (fp32 messages, fp64 emission) 5.5e-3 at 0.01, 4.0e-3 at 0.02, within
+// 9.5e-5 over 71 cases at 0.025-0.03.
+constexpr float geom_floor_t(int n, int k) {
+  return (k == 2 && n <= 12) ? 0.002f : n <= 15 ? 0.015f : 0.03f;
+}
 constexpr bool geom_precise_fits(int n, int k) {
   return (long long)geom_spb(n, k, kBwdP) * ((1LL << n) >> k) * 12 <= 150 * 1024;
 }

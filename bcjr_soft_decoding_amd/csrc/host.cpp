@@ -112,13 +112,9 @@ bcjr_status check_common(const bcjr_trellis* tr, int64_t B, int64_t L, int kind,
 
 bool temp_ok(float T) { return isfinite(T) && T > 0.0f; }
 
-// Shapes without fp64-message kernels (geom_precise_fits false) keep fp32 messages, with the
-// emission formed in fp64 below kPreciseBelowT; their gradient leaves 1e-3 below kMixedFloorT:
-// refused there.
-// Shapes with fp64-message kernels meet them down to kPreciseFloorT and are refused below it.
+// Each state size meets the tolerances down to its floor (geom_floor_t) and is refused below it.
 bool temp_supported(const bcjr_trellis* tr, float T) {
-  return geom_precise_fits(tr->state_bits, tr->bits_per_step) ? T >= kPreciseFloorT
-                                                               : T >= kMixedFloorT;
+  return T >= geom_floor_t(tr->state_bits, tr->bits_per_step);
 }
 
 // Workspaces are accessed with 16-byte vector loads and stores.

@@ -463,7 +463,7 @@ __device__ __forceinline__ void pin(T& x) {
 // Messages are carried in fp64 below kPreciseBelowT (geom.h), for every shape whose backward
 // message buffers (fp64 + fp32 per butterfly, single-buffered) fit in LDS; the other shapes keep
 // fp32 messages there with the fp64 emission (Mixed), and the host layer refuses temperatures
-// below kMixedFloorT for them. The fp64-message kernels use their own lane geometry
+// below their floor (geom_floor_t) for them. The fp64-message kernels use their own lane geometry
 // (kFwdP / kBwdP): fewer states per lane, since every message takes two registers.
 template <int n, int k>
 constexpr bool precise_fits() {

@@ -109,13 +109,13 @@ size_t bcjr_workspace_bytes(const bcjr_trellis* tr, int64_t B, int64_t L, int wh
  * kernels exist for every state size whose backward message buffers fit the 160 KiB of LDS,
  * i.e. n <= 15 at k = 2. For n = 16 (S = 2^16) the messages stay fp32 and below T = 0.05 only
  * the emission -(w - c)^2 / T and its sum with the message are formed in fp64 (w - c exactly),
- * which keeps the tolerances down to T = 0.004 for w and c of unit scale (inputs of scale lam
- * behave like unit-scale ones at T / lam^2); below T = 0.004 bcjr_forward and bcjr_backward
- * return BCJR_E_UNSUPPORTED for n = 16, before enqueueing anything. The fp64-message kernels
- * (n <= 15) meet the tolerances down to T = 0.002 (their exponentials and expectations are fp32;
- * at unit-scale inputs rare gradients reached 2e-3 at T = 0.0005): below T = 0.002 the soft
- * entry points (bcjr_forward, bcjr_backward, bcjr_forward_scan, bcjr_backward_scan) return
- * BCJR_E_UNSUPPORTED for every state size; viterbi_decode is the T -> 0 limit.
+ * Every state size meets the tolerances down to a floor (exponentials, posteriors and
+ * expectations are fp32 on every path, and near-tied paths amplify their rounding like 1/T,
+ * more often the more states there are): T = 0.002 for n <= 12, 0.015 for n = 13..15 and 0.03
+ * for n = 16, measured at w and c of unit scale (inputs of scale lam behave like unit-scale ones
+ * at T / lam^2). Below its floor the soft entry points (bcjr_forward, bcjr_backward,
+ * bcjr_forward_scan, bcjr_backward_scan) return BCJR_E_UNSUPPORTED before enqueueing anything;
+ * viterbi_decode is the T -> 0 limit.
  */
 bcjr_status bcjr_forward(const bcjr_trellis* tr, const float* w, int64_t B, int64_t L, float T,
                          float* w_hat, float* log_z, void* saved, void* ws, size_t ws_bytes,

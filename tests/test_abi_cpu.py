@@ -103,24 +103,22 @@ def test_forward_rejects_bad_arguments_without_device(lib):
     assert _fwd(lib, B=1, L=(1 << 40) + 1) == bcjr.BCJR_E_SHAPE
 
 
-def test_temperatures_below_the_fp64_threshold_need_fp64_kernels(lib):
-    """Below T = 0.05 the messages are fp64; the 2^16-state trellis has no such kernels (its
-    message buffers would not fit LDS), keeps fp32 messages with an fp64 emission down to
-    T = 0.004 and is refused below, before any device call."""
-    for T in (0.0039, 0.002, 1e-4):
-        assert _fwd(lib, n=16, T=T) == bcjr.BCJR_E_UNSUPPORTED
-        assert _fwd(lib, n=16, T=T, B=0, w=0, wh=0, lz=0, sv=0, ws=0, wsb=0) == bcjr.BCJR_E_UNSUPPORTED
+def test_temperatures_below_each_floor_are_refused(lib):
+    """Each state size meets the tolerances down to its floor (0.002 for n <= 12, 0.015 for
+    n = 13..15, 0.03 for n = 16, where no fp64-message kernels fit LDS); below it forward and
+    backward refuse before any device call, at and above it validation passes (the call then
+    needs a device: not made here, so only the status of a refused workspace is observed)."""
     P = ctypes.c_void_p
-    tr = bcjr.Trellis(16, 2, 1, 0x1000)
-    st = lib.bcjr_backward(ctypes.byref(tr), P(0x2000), 4, 8, 0.0035, P(0x3000), P(0x4000), None,
-                           P(0x5000), P(0x6000), P(0x7000), 1 << 40, None)
-    assert st == bcjr.BCJR_E_UNSUPPORTED
-    # at and above the floor, and for every smaller trellis, validation passes (the call then
-    # needs a device: not made here, so only the status of a refused workspace is observed)
-    for T in (0.004, 0.006, 0.01):
-        assert _fwd(lib, n=16, T=T, wsb=0) == bcjr.BCJR_E_WORKSPACE
-    for n in range(4, 16):
-        assert _fwd(lib, n=n, T=0.002, wsb=0) == bcjr.BCJR_E_WORKSPACE
+    for n, floor in ((16, 0.03), (15, 0.015), (13, 0.015), (12, 0.002), (4, 0.002)):
+        for T in (floor * 0.999, floor / 2, 1e-4):
+            assert _fwd(lib, n=n, T=T) == bcjr.BCJR_E_UNSUPPORTED
+            assert _fwd(lib, n=n, T=T, B=0, w=0, wh=0, lz=0, sv=0, ws=0, wsb=0) == bcjr.BCJR_E_UNSUPPORTED
+            tr = bcjr.Trellis(n, 2, 1, 0x1000)
+            st = lib.bcjr_backward(ctypes.byref(tr), P(0x2000), 4, 8, T, P(0x3000), P(0x4000), None,
+                                   P(0x5000), P(0x6000), P(0x7000), 1 << 40, None)
+            assert st == bcjr.BCJR_E_UNSUPPORTED
+        for T in (floor, floor * 1.5, 0.1):
+            assert _fwd(lib, n=n, T=T, wsb=0) == bcjr.BCJR_E_WORKSPACE
 
 
 def test_temperatures_below_the_fp64_floor_are_refused(lib):

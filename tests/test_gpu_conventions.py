@@ -65,7 +65,7 @@ CASES = [
     (8, 90, 40, 0.1, False),
     (8, 90, 40, 0.1, True),
     (12, 20, 30, 0.1, False),
-    (14, 5, 12, 0.005, False),
+    (14, 5, 12, 0.02, False),
     (16, 5, 10, 0.3, False),
 ]
 
@@ -227,7 +227,7 @@ def _sparse_on_stream(n, c, w, g, h, T):
             "grad_codebook": gc}
 
 
-@pytest.mark.parametrize("n,T,ckpt", [(8, 0.5, False), (8, 0.5, True), (15, 0.005, False),
+@pytest.mark.parametrize("n,T,ckpt", [(8, 0.5, False), (8, 0.5, True), (15, 0.02, False),
                                       (16, 0.3, False), (16, 0.3, True)])
 def test_zero_chains_overwrite_the_codebook_gradient(n, T, ckpt):
     """B = 0: the codebook gradient (a sum over no chains) is written as zeros over a

@@ -3,8 +3,9 @@ history layout and upstream log Z gradient (plus Viterbi bit-exactness), and the
 dense paths with random lengths, segment lengths and sizes. The cases are drawn once, at import,
 from fixed seeds, so every run checks the same ones. log Z is compared normwise like the other
 outputs: its fp32 error scales with the size of the summed terms, so a chain whose log Z happens
-to lie near zero would fail a purely relative test. At 2^16 states the library has no fp64-message
-kernels and refuses T below 0.004 (BCJR_E_UNSUPPORTED): such draws check the refusal."""
+to lie near zero would fail a purely relative test. Below each state size's temperature floor
+(0.002 for n <= 12, 0.015 for n = 13..15, 0.03 for n = 16) the library refuses the call
+(BCJR_E_UNSUPPORTED): such draws check the refusal."""
 import numpy as np
 import pytest
 import torch
@@ -70,7 +71,7 @@ def test_random_bitshift_shapes(n, B, L, T, ckpt, with_h, data_seed):
     w = (r.standard_normal((B, L)) * r.choice([0.3, 1.0, 2.0])).astype(np.float32)
     g = r.standard_normal((B, L)).astype(np.float32)
     h = r.standard_normal(B).astype(np.float32) if with_h else None
-    if n == 16 and T < 0.004:
+    if T < (0.002 if n <= 12 else 0.015 if n <= 15 else 0.03):
         assert_refused(n, 2, c, w, T, g)
         return
     ref = oracle.sparse_forward(n, 2, c, w, T)

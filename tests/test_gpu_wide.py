@@ -38,11 +38,11 @@ CASES = [
     (16, 300, 24, 0.3, ("full", "ckpt")),
     (16, 270, 7, 0.05, ("full", "ckpt")),   # ragged checkpoint segments (3, 3, 1)
     (15, 280, 20, 0.2, ("full",)),           # 2 blocks per lane
-    (15, 280, 20, 0.005, ("full", "ckpt")),  # fp64 messages
-    (14, 300, 16, 0.005, ("full",)),         # fp64 messages, 1 block per lane
+    (15, 280, 20, 0.02, ("full", "ckpt")),   # fp64 messages
+    (14, 300, 16, 0.02, ("full",)),          # fp64 messages, 1 block per lane
     (16, 3, 1, 0.3, ("full", "ckpt")),       # L = 1: no recursion step at all
     (16, 3, 2, 0.3, ("full", "ckpt")),       # L = 2: one step each way
-    (15, 2, 1, 0.005, ("full", "ckpt")),     # L = 1 with fp64 messages
+    (15, 2, 1, 0.02, ("full", "ckpt")),      # L = 1 with fp64 messages
 ]
 
 
@@ -63,7 +63,7 @@ def test_wide_chains_match_oracle(n, B, L, T, hists):
         assert_normwise(got["grad_codebook"], rb["grad_codebook"], RTOL_GRAD, f"{hist} grad_c")
 
 
-@pytest.mark.parametrize("n,B,L,T", [(14, 256, 16, 0.005), (16, 260, 9, 0.3)])
+@pytest.mark.parametrize("n,B,L,T", [(14, 256, 16, 0.02), (16, 260, 9, 0.3)])
 def test_wide_bitwise_deterministic(n, B, L, T):
     """Repeated runs (one with a NaN-poisoned workspace) agree bitwise. The fp64-message chains
     mix double and float chain reductions; the fp32 ones read their accumulator rows back."""
@@ -88,11 +88,11 @@ def test_wide_bitwise_deterministic(n, B, L, T):
             np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [0.0039, 0.002, 0.001])
-def test_2_16_states_below_0004_refused(T):
+@pytest.mark.parametrize("T", [0.0299, 0.02, 0.01, 0.004, 0.001])
+def test_2_16_states_below_the_floor_refused(T):
     """The 2^16-state trellis has no fp64-message kernels (their two message buffers would not
-    fit LDS); with fp32 messages and the fp64 emission its gradient left 1e-3 at T = 0.002 on a
-    random input: forward and backward refuse temperatures below 0.004 with
+    fit LDS); with fp32 messages and the fp64 emission randomized sweeps put rare gradients at
+    4e-3 at T = 0.02 and 5.5e-3 at 0.01: forward and backward refuse temperatures below 0.03 with
     BCJR_E_UNSUPPORTED, enqueue nothing and leave their outputs untouched."""
     n, B, L = 16, 5, 24
     log_case(f"n=16 refused T={T}")
@@ -103,7 +103,7 @@ def test_2_16_states_below_0004_refused(T):
 
 
 @pytest.mark.parametrize("seed,B,L", [(7500, 5, 24), (7600, 6, 40)])
-@pytest.mark.parametrize("T", [0.02, 0.0099, 0.006, 0.004])
+@pytest.mark.parametrize("T", [0.045, 0.035, 0.03])
 def test_2_16_states_below_threshold_fp64_emission(T, seed, B, L):
     """Below T = 0.05 the 2^16-state kernels keep fp32 messages and form the emission in fp64
     (w - c exactly, its square and its sum with the message in fp64). Against the oracle, both
@@ -126,10 +126,10 @@ def test_2_16_states_below_threshold_fp64_emission(T, seed, B, L):
 
 
 def test_2_16_states_at_the_threshold_match_oracle():
-    """T = 0.05 exactly, the lowest temperature of the fp32 emission at 2^16 states, and T = 0.01
-    (the fp64 emission), against the oracle on the input that erred by 0.51 at T = 0.002 with the
+    """T = 0.05 exactly, the lowest temperature of the fp32 emission at 2^16 states, and T = 0.03
+    (the fp64 emission at the floor), against the oracle on the input that erred by 0.51 at T = 0.002 with the
     fp32 emission."""
-    for T in (0.05, 0.01):
+    for T in (0.05, 0.03):
         _threshold_case(T)
 
 
